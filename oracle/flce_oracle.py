@@ -1,0 +1,146 @@
+"""CPU oracle for fused linear cross-entropy (FLCE).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, links or
+runs this module; only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may.  It shares no code with the HIP
+library: the only common dependency is the seeded input generator
+(``flce_inputs``), which holds none of the method's arithmetic.
+
+What it computes is the plain, materialised definition that FLCE reaches
+exactly (up to rounding order): the pages present FLCE as a memory
+optimisation that yields the same loss and gradients as projecting every
+token through the LM head and applying softmax cross-entropy
+("Fused Linear Cross-Entropy", 42jerrykim.github.io, introduction and the
+section on the core idea; the "Unsloth deep architecture" page,
+techknowgenie.com, describes its streaming CE kernel as exact, not an
+approximation).  So the oracle materialises the full [N,V] logits in fp64.
+
+Notation: hidden states x[N,H], LM-head weight W[V,H] (row-major, one row per
+vocabulary id, as in the code sample of the "core idea" section), targets
+t[N] (int64 ids in [0,V)).
+
+Readings taken where the pages are silent or disagree:
+  * reduction is the mean over all N tokens, and dx, dW carry the same 1/N:
+    the code sample of the "core idea" section sums per chunk and divides
+    loss, dx and dw by the global token count at the end;
+  * no bias, no ignore_index, no label smoothing (none is mentioned; the
+    projection in the code sample has no bias);
+  * W is [V,H] (the 128K-context guide at sigco.tistory.com prints an [H,V]
+    weight in its chunked-CE snippet; the [V,H] layout of the FLCE page is
+    taken).
+Every function below is pinned by tests against closed forms, invariants,
+finite differences and a hand-derived worked example (tests/golden).
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable
+
+import numpy as np
+
+__all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce",
+           "flce_rows", "logits_bytes"]
+
+
+def widen(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage form -> fp64, exactly (bf16 bit patterns or fp32 values)."""
+    if dtype == "bf16":
+        bits = np.ascontiguousarray(arr, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "fp32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "fp64":
+        return np.asarray(arr, dtype=np.float64)
+    raise ValueError(dtype)
+
+
+def logits(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Z = x W^T, [N,V]: the LM-head projection (FLCE page, core idea, step 1)."""
+    return x @ W.T
+
+
+def row_logsumexp(Z: np.ndarray) -> np.ndarray:
+    """lse_n = m_n + ln sum_v exp(Z[n,v] - m_n), m_n = max_v Z[n,v].
+
+    The log-sum-exp term of the cross-entropy equation on the Unsloth page
+    ("streaming chunked Fast CrossEntropy loss kernel"); the max is
+    subtracted first, as that page's online-softmax description keeps a
+    running maximum for numerical stability.
+    """
+    m = Z.max(axis=1)
+    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+
+
+def row_losses(Z: np.ndarray, t: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """L_n = -Z[n, t_n] + lse_n (Unsloth page, cross-entropy loss equation)."""
+    return lse - Z[np.arange(Z.shape[0]), t]
+
+
+def dlogits(Z: np.ndarray, t: np.ndarray, lse: np.ndarray, n_total: int) -> np.ndarray:
+    """G = (softmax(Z) - onehot(t)) / N.
+
+    dL/dz_i = softmax(z)_i - [i = y] (Unsloth page, gradient equation; the
+    FLCE page's step 2 overwrites the logits with softmax - one_hot), scaled
+    by 1/N for the mean reduction (FLCE page, code sample, final division by
+    the token count).
+    """
+    G = np.exp(Z - lse[:, None])
+    G[np.arange(Z.shape[0]), t] -= 1.0
+    G /= float(n_total)
+    return G
+
+
+def flce(x: np.ndarray, W: np.ndarray, t: np.ndarray) -> Dict[str, np.ndarray]:
+    """The whole materialised computation in fp64.
+
+    Returns loss (mean over N), dx = G W [N,H], dW = G^T x [V,H], and the
+    per-row lse [N] and losses [N].  Steps 3 and 4 of the FLCE page's core
+    idea (dx = dlogits x weight; dw = dlogits^T x hidden), here over all N at
+    once instead of per chunk.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    N = x.shape[0]
+    if N == 0:
+        raise ValueError("N must be positive (the mean over zero tokens is undefined)")
+    if t.min() < 0 or t.max() >= W.shape[0]:
+        raise ValueError("targets out of range")
+    Z = logits(x, W)
+    lse = row_logsumexp(Z)
+    losses = row_losses(Z, t, lse)
+    G = dlogits(Z, t, lse, N)
+    del Z
+    dx = G @ W
+    dW = G.T @ x
+    return {"loss": float(losses.mean()), "dx": dx, "dW": dW, "lse": lse, "losses": losses}
+
+
+def flce_rows(x: np.ndarray, W: np.ndarray, t: np.ndarray, rows: Iterable[int],
+              n_total: int) -> Dict[str, np.ndarray]:
+    """lse_n, loss_n and dx_n for selected token rows, computed one row at a time.
+
+    The same definition as ``flce`` restricted to single rows (a row of dx
+    depends only on that token's logits row), so full-size problems can be
+    checked on sampled rows.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    rows = list(rows)
+    lse = np.empty(len(rows))
+    loss = np.empty(len(rows))
+    dx = np.empty((len(rows), W.shape[1]))
+    for i, n in enumerate(rows):
+        xn = np.asarray(x[n], dtype=np.float64)
+        z = W @ xn
+        m = z.max()
+        lse[i] = m + np.log(np.exp(z - m).sum())
+        loss[i] = lse[i] - z[t[n]]
+        g = np.exp(z - lse[i])
+        g[t[n]] -= 1.0
+        g /= float(n_total)
+        dx[i] = g @ W
+    return {"lse": lse, "loss": loss, "dx": dx}
+
+
+def logits_bytes(n_tokens: int, vocab: int, bytes_per_elem: int) -> int:
+    """Size of a materialised [N,V] logits tensor, the footprint FLCE avoids."""
+    return int(n_tokens) * int(vocab) * int(bytes_per_elem)

@@ -1,0 +1,196 @@
+"""Pins for the FLCE oracle: checks that tie it to facts other than itself.
+
+Each ``check_*`` takes an ``flce(x, W, t) -> dict`` implementation (the
+oracle, or a copy of it with a planted mistake) and raises AssertionError
+when the implementation disagrees with
+
+  * hand-derived worked examples (tests/golden/worked_examples.json),
+  * closed forms (W = 0; two classes reduce to softplus),
+  * central finite differences of the loss in fp64,
+  * invariants of the definition (dlogits rows sum to zero, dW column sums
+    vanish, <x,dx> = <W,dW>, per-row logit shift, permutations),
+  * an independent library routine (torch.nn.functional.cross_entropy with
+    autograd, fp64, CPU).
+
+The definition being pinned: loss = mean_n(lse_n - z[n,t_n]),
+G = (softmax(z) - onehot(t))/N, dx = G W, dW = G^T x with z = x W^T
+(cross-entropy and gradient equations of the "Unsloth deep architecture"
+page, streaming Fast CrossEntropy section; mean reduction with 1/N on the
+gradients from the code sample of the "core idea" section of the "Fused
+Linear Cross-Entropy" page).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _eval(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"log": math.log, "exp": math.exp}))
+
+
+def _mat(rows):
+    return np.array([[_eval(e) for e in r] for r in rows], dtype=np.float64)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert np.allclose(a, b, rtol=rtol, atol=atol), \
+        f"{what}: max abs diff {np.max(np.abs(a - b))}"
+
+
+def check_worked_examples(flce):
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        x, W = _mat(e["x"]), _mat(e["W"])
+        t = np.array(e["t"], dtype=np.int64)
+        r = flce(x, W, t)
+        _close(r["loss"], _eval(e["loss"]), 1e-12, 1e-12, e["name"] + " loss")
+        _close(r["dx"], _mat(e["dx"]), 1e-12, 1e-12, e["name"] + " dx")
+        _close(r["dW"], _mat(e["dW"]), 1e-12, 1e-12, e["name"] + " dW")
+
+
+def check_zero_weight(flce, N=37, H=11, V=29, seed=0):
+    """W = 0: every logit is 0, softmax is uniform 1/V.
+
+    loss = ln V exactly; dx = G W = 0; dW[v] = (1/V) mean_n x_n - (1/N) sum_{n: t_n = v} x_n.
+    """
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    t = rng.integers(0, V, N)
+    t[:3] = [0, V - 1, 5]
+    r = flce(x, np.zeros((V, H)), t)
+    _close(r["loss"], math.log(V), 1e-15, 0, "W=0 loss")
+    assert np.all(r["dx"] == 0.0), "W=0 dx must be exactly 0"
+    expect = np.tile(x.mean(axis=0) / V, (V, 1))
+    for n in range(N):
+        expect[t[n]] -= x[n] / N
+    _close(r["dW"], expect, 1e-12, 1e-14, "W=0 dW")
+
+
+def check_two_classes(flce, N=50, H=7, seed=1):
+    """V = 2: the per-row loss is softplus(z_other - z_target) = log(1 + e^d)."""
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((2, H))
+    t = rng.integers(0, 2, N)
+    z = np.einsum("nh,vh->nv", x, W)
+    d = z[np.arange(N), 1 - t] - z[np.arange(N), t]
+    want = np.logaddexp(0.0, d).mean()
+    r = flce(x, W, t)
+    _close(r["loss"], want, 1e-13, 0, "V=2 softplus")
+
+
+def _loss_only(flce, x, W, t):
+    return flce(x, W, t)["loss"]
+
+
+def check_finite_differences(flce, N=3, H=5, V=7, seed=2, eps=1e-6):
+    """dx and dW against central differences of the loss (fp64, O(eps^2) error)."""
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.5
+    t = rng.integers(0, V, N)
+    r = flce(x, W, t)
+    fdx = np.zeros_like(x)
+    for i in range(N):
+        for j in range(H):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += eps
+            xm[i, j] -= eps
+            fdx[i, j] = (_loss_only(flce, xp, W, t) - _loss_only(flce, xm, W, t)) / (2 * eps)
+    fdW = np.zeros_like(W)
+    for i in range(V):
+        for j in range(H):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += eps
+            Wm[i, j] -= eps
+            fdW[i, j] = (_loss_only(flce, x, Wp, t) - _loss_only(flce, x, Wm, t)) / (2 * eps)
+    _close(r["dx"], fdx, 1e-6, 1e-9, "dx vs finite differences")
+    _close(r["dW"], fdW, 1e-6, 1e-9, "dW vs finite differences")
+
+
+def check_invariants(flce, N=40, H=16, V=33, seed=3):
+    """Row sums of G vanish, so dW's column sums vanish and <x,dx> = <W,dW>."""
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.3
+    t = rng.integers(0, V, N)
+    r = flce(x, W, t)
+    scale = np.abs(r["dW"]).max()
+    assert np.abs(r["dW"].sum(axis=0)).max() <= 1e-13 * max(scale, 1.0) * V, "dW column sums"
+    a = float(np.sum(x * r["dx"]))
+    b = float(np.sum(W * r["dW"]))
+    _close(a, b, 1e-12, 1e-15, "<x,dx> vs <W,dW>")
+    # lse is at least the row max and at most max + ln V
+    z = x @ W.T
+    assert np.all(r["lse"] >= z.max(axis=1) - 1e-12)
+    assert np.all(r["lse"] <= z.max(axis=1) + math.log(V) + 1e-12)
+
+
+def check_shift_invariance(flce, N=20, H=9, V=17, seed=4, shift=300.0):
+    """W -> W + 1 u^T adds <x_n, u> to every logit of row n: nothing changes."""
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.2
+    t = rng.integers(0, V, N)
+    u = rng.standard_normal(H) * shift
+    r0 = flce(x, W, t)
+    r1 = flce(x, W + u[None, :], t)
+    _close(r1["loss"], r0["loss"], 1e-9, 0, "shifted loss")
+    _close(r1["dW"], r0["dW"], 1e-9, 1e-12, "shifted dW")
+    _close(r1["dx"], r0["dx"], 1e-7, 1e-9, "shifted dx")
+
+
+def check_permutations(flce, N=25, H=6, V=19, seed=5):
+    """Permuting tokens permutes dx; permuting vocabulary rows (and relabelling targets) permutes dW."""
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.4
+    t = rng.integers(0, V, N)
+    r = flce(x, W, t)
+    pn = rng.permutation(N)
+    rn = flce(x[pn], W, t[pn])
+    _close(rn["dx"], r["dx"][pn], 1e-12, 1e-15, "token permutation dx")
+    _close(rn["loss"], r["loss"], 1e-13, 0, "token permutation loss")
+    pv = rng.permutation(V)
+    inv = np.argsort(pv)
+    rv = flce(x, W[pv], inv[t])
+    _close(rv["dW"], r["dW"][pv], 1e-12, 1e-15, "vocab permutation dW")
+    _close(rv["dx"], r["dx"], 1e-12, 1e-15, "vocab permutation dx")
+
+
+def check_torch_autograd(flce, N=31, H=12, V=45, seed=6):
+    """Independent library routine: torch cross_entropy + autograd in fp64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.5
+    t = rng.integers(0, V, N)
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    loss = F.cross_entropy(xt @ Wt.T, torch.tensor(t), reduction="mean")
+    loss.backward()
+    r = flce(x, W, t)
+    _close(r["loss"], loss.item(), 1e-13, 0, "torch loss")
+    _close(r["dx"], xt.grad.numpy(), 1e-11, 1e-15, "torch dx")
+    _close(r["dW"], Wt.grad.numpy(), 1e-11, 1e-15, "torch dW")
+
+
+ALL_CHECKS = [check_worked_examples, check_zero_weight, check_two_classes,
+              check_finite_differences, check_invariants, check_shift_invariance,
+              check_permutations, check_torch_autograd]

@@ -1,0 +1,132 @@
+"""The CPU oracle against its pins (CPU only).
+
+Also plants plausible mistakes in copies of the oracle and checks that at
+least one pin catches each one, so the pins are known to be sensitive.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import flce_oracle as fo
+import oracle_pins as pins
+from flce_inputs import make_inputs, WORKLOADS
+
+
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check(oracle.flce)
+
+
+# ---- planted mistakes ------------------------------------------------------
+
+def _mutant(kind):
+    def flce(x, W, t):
+        x = np.asarray(x, dtype=np.float64)
+        W = np.asarray(W, dtype=np.float64)
+        t = np.asarray(t, dtype=np.int64)
+        N, V = x.shape[0], W.shape[0]
+        tt = (t + 1) % V if kind == "target_off_by_one" else t
+        Z = x @ W.T
+        if kind == "no_max_subtraction":
+            lse = np.log(np.exp(Z).sum(axis=1))
+        elif kind == "lse_missing_log":
+            m = Z.max(axis=1)
+            lse = m + np.exp(Z - m[:, None]).sum(axis=1)
+        else:
+            lse = fo.row_logsumexp(Z)
+        losses = lse - Z[np.arange(N), tt]
+        loss = losses.sum() if kind == "sum_not_mean" else losses.mean()
+        G = np.exp(Z - lse[:, None])
+        if kind == "no_onehot":
+            pass
+        elif kind == "onehot_wrong_sign":
+            G[np.arange(N), tt] += 1.0
+        else:
+            G[np.arange(N), tt] -= 1.0
+        if kind != "no_1_over_N":
+            G /= N
+        dx = G @ W
+        if kind == "dx_uses_WT_rows_reversed":
+            dx = G @ W[::-1]
+        dW = G.T @ x
+        if kind == "dW_tokens_reversed":
+            dW = G.T @ x[::-1]
+        return {"loss": float(loss), "dx": dx, "dW": dW, "lse": lse, "losses": losses}
+    return flce
+
+
+MUTANTS = ["target_off_by_one", "no_max_subtraction", "lse_missing_log", "sum_not_mean",
+           "no_onehot", "onehot_wrong_sign", "no_1_over_N", "dx_uses_WT_rows_reversed",
+           "dW_tokens_reversed"]
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_pins_catch_planted_mistake(kind):
+    bad = _mutant(kind)
+    caught = []
+    with np.errstate(all="ignore"):
+        for check in pins.ALL_CHECKS:
+            try:
+                check(bad)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {kind!r}"
+
+
+def test_unmutated_copy_passes_all_pins():
+    good = _mutant("none")
+    for check in pins.ALL_CHECKS:
+        check(good)
+
+
+# ---- other properties of the oracle ---------------------------------------
+
+def test_rows_match_full():
+    d = make_inputs(64, 32, 300, "bf16", seed=11)
+    x = oracle.widen(d["x"], "bf16")
+    W = oracle.widen(d["W"], "bf16")
+    r = oracle.flce(x, W, d["t"])
+    rows = [0, 7, 63]
+    rr = oracle.flce_rows(x, W, d["t"], rows, 64)
+    np.testing.assert_allclose(rr["lse"], r["lse"][rows], rtol=1e-14)
+    np.testing.assert_allclose(rr["loss"], r["losses"][rows], rtol=1e-13)
+    np.testing.assert_allclose(rr["dx"], r["dx"][rows], rtol=1e-11, atol=1e-17)
+
+
+def test_statistical_expectation_of_loss():
+    """x ~ N(0,1), W ~ N(0,0.02^2): logits ~ N(0, 4e-4 |x|^2), so E[loss] ~ ln V + 2e-4 H."""
+    w = WORKLOADS["tiny_fp32"]
+    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
+    r = oracle.flce(oracle.widen(d["x"], "fp32"), oracle.widen(d["W"], "fp32"), d["t"])
+    assert abs(r["loss"] - (math.log(w.V) + 2e-4 * w.H)) < 0.1
+
+
+def test_widen_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x4049], dtype=np.uint16)
+    got = oracle.widen(bits, "bf16")
+    assert got[0] == 1.0 and got[1] == -1.0
+    assert got[2] == 2.0 ** -133      # smallest bf16 subnormal
+    assert got[3] == (2 - 2 ** -7) * 2.0 ** 127
+    assert got[4] == 3.140625
+
+
+def test_rejects_empty_and_bad_targets():
+    with pytest.raises(ValueError):
+        oracle.flce(np.zeros((0, 3)), np.zeros((4, 3)), np.zeros(0, dtype=np.int64))
+    with pytest.raises(ValueError):
+        oracle.flce(np.zeros((2, 3)), np.zeros((4, 3)), np.array([0, 4]))
+
+
+def test_page_logit_sizes():
+    with open(os.path.join(pins.GOLDEN, "page_logit_sizes.json")) as f:
+        figs = json.load(f)["figures"]
+    for fgr in figs:
+        b = oracle.logits_bytes(fgr["tokens"], fgr["vocab"], fgr["bytes_per_elem"])
+        if "elements" in fgr:
+            assert fgr["tokens"] * fgr["vocab"] == fgr["elements"], fgr["cite"]
+        unit = 1e9 if fgr["unit"] == "GB" else 2.0 ** 30
+        assert abs(b / unit - fgr["printed"]) <= fgr["rel_tol"] * fgr["printed"], fgr["cite"]
