@@ -1,0 +1,146 @@
+/*
+ * flce.h - C ABI of the MI355X (gfx950) fused linear cross-entropy library.
+ *
+ * Fused linear cross-entropy (FLCE) projects token hidden states through the
+ * LM-head weight and applies softmax cross-entropy, forward and backward in
+ * one call, without materialising the [N,V] logits: tokens are processed in
+ * chunks, each chunk's logits buffer is overwritten in place by its
+ * gradient, dx is produced per chunk and dW is accumulated across chunks
+ * (the four-step loop of the core-idea section of the "Fused Linear
+ * Cross-Entropy" page, 42jerrykim.github.io).  Because it is the last layer,
+ * the gradients are finished inside the forward call.
+ *
+ * For x[N,H], W[V,H] and targets t[N] the call returns
+ *   loss = (1/N) sum_n ( lse_n - z[n,t_n] ),  z = x W^T,  lse_n = ln sum_v e^{z[n,v]}
+ *   dx   = G W,   dW = G^T x,   G = (softmax(z) - onehot(t)) / N
+ * (loss and gradient equations of the "Unsloth deep architecture" page,
+ * techknowgenie.com, streaming Fast CrossEntropy section; mean reduction and
+ * the 1/N on both gradients as in the code sample of the FLCE page).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are caller-owned DEVICE pointers on the handle's device,
+ *    row-major and contiguous, 16-byte aligned.
+ *  - `stream` is a hipStream_t (passed as void*).  Every kernel is enqueued
+ *    on it and the call returns after enqueueing: no host synchronisation,
+ *    no use of the null stream by the library itself (the stream/event
+ *    ordering rules of the async continuous-batching page, pogovet.com).
+ *    Results are valid once the stream reaches that point.
+ *  - Validation happens before any launch; a call that returns an error
+ *    writes nothing.  Nothing aborts and no exception crosses the ABI.
+ *  - A handle must not be used by two calls at the same time.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = 1,   /* null pointer, N/H/V < 1, bad enum value */
+  FLCE_ERR_UNSUPPORTED = 2,   /* H % 8 != 0, misaligned pointer, dtype combination not built, size limits */
+  FLCE_ERR_OOM = 3,           /* workspace allocation failed or exceeds cfg.workspace_limit */
+  FLCE_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  FLCE_ERR_DATA = 5           /* flce_check: a target id was outside [0, V) */
+} flce_status_t;
+
+typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype_t;
+
+typedef enum {
+  FLCE_CHUNKED = 0,           /* token chunks; one [C,V] buffer overwritten in place by dlogits */
+  FLCE_FUSED = 1              /* reserved for the two-pass fused variant (not built: FLCE_ERR_UNSUPPORTED) */
+} flce_variant_t;
+
+typedef struct {
+  int32_t in_dtype;           /* dtype of x and W: FLCE_BF16 or FLCE_FP32 */
+  int32_t dx_dtype;           /* dtype of dx: FLCE_BF16 (bf16 inputs only) or FLCE_FP32 */
+  int32_t dw_dtype;           /* dtype of dW: FLCE_BF16 (bf16 inputs only) or FLCE_FP32 */
+  int32_t variant;            /* flce_variant_t */
+  int32_t device;             /* HIP device ordinal the handle and its workspace belong to */
+  int32_t reserved;           /* must be 0 */
+  int64_t workspace_limit;    /* bytes; 0 = no limit.  A plan needing more fails with FLCE_ERR_OOM */
+} flce_config_t;
+
+typedef struct flce_handle_s* flce_handle_t;
+
+/* Creates a handle.  No device memory is allocated yet.
+ * Errors: INVALID_ARG (null cfg/out, bad enum), UNSUPPORTED (fp32 inputs with a bf16 output),
+ *         HIP (device ordinal not usable). */
+flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
+
+/* Frees the handle's workspace (device-synchronising) and the handle.  NULL is a no-op. */
+flce_status_t flce_destroy(flce_handle_t h);
+
+/* One fused forward+backward pass.
+ *   x       [N,H]  cfg.in_dtype, read-only
+ *   W       [V,H]  cfg.in_dtype, read-only
+ *   targets [N]    int64, each expected in [0,V).  An id outside that range never faults: that
+ *                  token's loss is NaN (so `loss` is NaN), its gradient row is the plain softmax,
+ *                  and a device flag is raised that flce_check reports as FLCE_ERR_DATA.
+ *   chunk          tokens per chunk; <= 0 selects the automatic size (flce_effective_chunk)
+ *   loss    [1]    fp32, overwritten with the mean loss over the N tokens
+ *   dx      [N,H]  cfg.dx_dtype, overwritten (must not alias x)
+ *   dW      [V,H]  cfg.dw_dtype, overwritten (must not alias W)
+ * The workspace grows on demand (hipMalloc/hipFree, which synchronise the device); call
+ * flce_reserve beforehand to keep allocation out of timed or captured regions.
+ * Errors: INVALID_ARG, UNSUPPORTED, OOM (outputs untouched), HIP. */
+flce_status_t flce_forward_backward(flce_handle_t h, const void* x, const void* W,
+                                    const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                    int64_t chunk, float* loss, void* dx, void* dW, void* stream);
+
+/* As flce_forward_backward, and additionally writes the per-token log-sum-exp
+ * lse_n = ln sum_v exp(z[n,v]) (fp32, [N]) to `lse` when it is not NULL. */
+flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,
+                                       const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                       int64_t chunk, float* loss, void* dx, void* dW, float* lse,
+                                       void* stream);
+
+/* Token chunk the call would use: chunk clamped to [1, N] when positive; for chunk <= 0 the
+ * size rule of the FLCE page's trade-offs section, next_pow2(ceil(N / ceil(V/H))), raised to at
+ * least 2048 tokens (below that the per-chunk re-read of W makes the path HBM-bound on MI355X)
+ * and at most 8192, then clamped to N.  Returns 0 for invalid sizes. */
+int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk);
+
+/* Workspace bytes a call with these sizes needs (0 for invalid sizes). */
+size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk);
+
+/* Allocates the workspace for these sizes now (no-op if already large enough).
+ * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. */
+flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk);
+
+/* Synchronises `stream`, then reports and clears the device-side data flag:
+ * FLCE_ERR_DATA if any call since the last check saw a target outside [0,V), else FLCE_OK. */
+flce_status_t flce_check(flce_handle_t h, void* stream);
+
+/* ---- per-kernel timing (tracing) ----------------------------------------------------
+ * When enabled, every launch a call makes is bracketed by HIP events recorded on the
+ * caller's stream, so each kernel's duration is the time between the event before it and
+ * the event after it on that stream.  Enabling (or disabling) resets the statistics. */
+typedef struct {
+  char name[32];          /* kernel name, e.g. "logits_lse", "dx", "dw" */
+  int64_t launches;       /* launches timed since the last reset */
+  double total_ms;        /* summed durations of those launches */
+  double flops;           /* summed algorithmic flops: 2*rows*V*H for each GEMM launch, 0 otherwise */
+  double bytes;           /* summed algorithmic HBM bytes (each operand read once, each result written once) */
+} flce_kernel_stat_t;
+
+/* Errors: INVALID_ARG (null handle). */
+flce_status_t flce_profile_enable(flce_handle_t h, int enable);
+
+/* Synchronises on the recorded events, folds them into the statistics and copies up to
+ * `capacity` entries (one per kernel that ran) into `out`; `*count` receives the number of
+ * entries available.  Errors: INVALID_ARG, HIP. */
+flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int capacity, int* count);
+
+/* Static description of a status code. */
+const char* flce_status_string(flce_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

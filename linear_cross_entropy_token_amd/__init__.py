@@ -1,0 +1,241 @@
+"""MI355X-native fused linear cross-entropy (FLCE).
+
+A thin Python binding over ``libflce.so`` (hand-written HIP kernels for
+gfx950 behind the C ABI declared in ``include/flce.h``).  The functions
+``flce_create``, ``flce_forward_backward`` ... mirror the C entry points one
+to one and only marshal arguments; every step of the computation runs in the
+library's kernels.  ``FusedLinearCrossEntropy`` is a convenience wrapper that
+takes torch device tensors (torch supplies device memory and the stream).
+
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "FLCE_BF16", "FLCE_FP32", "FLCE_CHUNKED", "FLCE_FUSED", "STATUS", "FlceError", "Config",
+    "library_path", "load_library", "flce_create", "flce_destroy", "flce_forward_backward",
+    "flce_forward_backward_ex", "flce_effective_chunk", "flce_workspace_bytes", "flce_reserve",
+    "flce_check", "flce_status_string", "flce_profile_enable", "flce_profile_read", "KernelStat",
+    "FusedLinearCrossEntropy",
+]
+
+FLCE_BF16, FLCE_FP32 = 0, 1
+FLCE_CHUNKED, FLCE_FUSED = 0, 1
+STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_ARG", 2: "FLCE_ERR_UNSUPPORTED", 3: "FLCE_ERR_OOM",
+          4: "FLCE_ERR_HIP", 5: "FLCE_ERR_DATA"}
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {flce_status_string(status)}" if what else flce_status_string(status))
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("in_dtype", ctypes.c_int32), ("dx_dtype", ctypes.c_int32),
+                ("dw_dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("device", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_limit", ctypes.c_int64)]
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads libflce.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with `python -m linear_cross_entropy_token_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.flce_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(vp)]
+    lib.flce_create.restype = i32
+    lib.flce_destroy.argtypes = [vp]
+    lib.flce_destroy.restype = i32
+    lib.flce_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp]
+    lib.flce_forward_backward.restype = i32
+    lib.flce_forward_backward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.flce_forward_backward_ex.restype = i32
+    lib.flce_effective_chunk.argtypes = [i64, i64, i64, i64]
+    lib.flce_effective_chunk.restype = i64
+    lib.flce_workspace_bytes.argtypes = [vp, i64, i64, i64, i64]
+    lib.flce_workspace_bytes.restype = ctypes.c_size_t
+    lib.flce_reserve.argtypes = [vp, i64, i64, i64, i64]
+    lib.flce_reserve.restype = i32
+    lib.flce_check.argtypes = [vp, vp]
+    lib.flce_check.restype = i32
+    lib.flce_profile_enable.argtypes = [vp, i32]
+    lib.flce_profile_enable.restype = i32
+    lib.flce_profile_read.argtypes = [vp, ctypes.POINTER(KernelStat), i32, ctypes.POINTER(i32)]
+    lib.flce_profile_read.restype = i32
+    lib.flce_status_string.argtypes = [i32]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---- one-to-one wrappers of the C entry points (plain ints/pointers) -------
+
+def flce_status_string(status: int) -> str:
+    return load_library().flce_status_string(int(status)).decode()
+
+
+def flce_create(cfg: Config) -> int:
+    h = ctypes.c_void_p()
+    st = load_library().flce_create(ctypes.byref(cfg), ctypes.byref(h))
+    if st != 0:
+        raise FlceError(st, "flce_create")
+    return h.value
+
+
+def flce_destroy(handle: int) -> int:
+    return load_library().flce_destroy(handle)
+
+
+def flce_forward_backward(handle, x, W, targets, N, H, V, chunk, loss, dx, dW, stream) -> int:
+    return load_library().flce_forward_backward(handle, x, W, targets, N, H, V, chunk, loss, dx, dW, stream)
+
+
+def flce_forward_backward_ex(handle, x, W, targets, N, H, V, chunk, loss, dx, dW, lse, stream) -> int:
+    return load_library().flce_forward_backward_ex(handle, x, W, targets, N, H, V, chunk, loss, dx, dW,
+                                                   lse, stream)
+
+
+def flce_effective_chunk(N, H, V, chunk) -> int:
+    return load_library().flce_effective_chunk(N, H, V, chunk)
+
+
+def flce_workspace_bytes(handle, N, H, V, chunk) -> int:
+    return load_library().flce_workspace_bytes(handle, N, H, V, chunk)
+
+
+def flce_reserve(handle, N, H, V, chunk) -> int:
+    return load_library().flce_reserve(handle, N, H, V, chunk)
+
+
+def flce_check(handle, stream) -> int:
+    return load_library().flce_check(handle, stream)
+
+
+def flce_profile_enable(handle, enable) -> int:
+    return load_library().flce_profile_enable(handle, int(enable))
+
+
+def flce_profile_read(handle):
+    """Returns (status, {kernel name: dict(launches, total_ms, flops, bytes)})."""
+    arr = (KernelStat * 16)()
+    n = ctypes.c_int()
+    st = load_library().flce_profile_read(handle, arr, 16, ctypes.byref(n))
+    out = {}
+    for i in range(min(n.value, 16)):
+        k = arr[i]
+        out[k.name.decode()] = {"launches": k.launches, "total_ms": k.total_ms, "flops": k.flops,
+                                "bytes": k.bytes}
+    return st, out
+
+
+# ---- torch convenience wrapper -----------------------------------------------
+
+def _dt_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return FLCE_BF16
+    if dtype == torch.float32:
+        return FLCE_FP32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+class FusedLinearCrossEntropy:
+    """Owns one library handle; takes torch device tensors.
+
+    ``forward_backward(x, W, t)`` returns ``(loss, dx, dW)`` (and ``lse`` if
+    asked): loss is a 0-d fp32 device tensor, dx/dW have the configured dtypes.
+    Work is enqueued on torch's current stream of the tensors' device.
+    """
+
+    def __init__(self, in_dtype=None, dx_dtype=None, dw_dtype=None, device: int = 0,
+                 variant: int = FLCE_CHUNKED, workspace_limit: int = 0):
+        import torch
+        in_dtype = in_dtype or torch.bfloat16
+        self.in_dtype = in_dtype
+        self.dx_dtype = dx_dtype or in_dtype
+        self.dw_dtype = dw_dtype or in_dtype
+        self.device = device
+        cfg = Config(_dt_code(in_dtype), _dt_code(self.dx_dtype), _dt_code(self.dw_dtype), variant,
+                     device, 0, workspace_limit)
+        self.handle = flce_create(cfg)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            flce_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, N, H, V, chunk=0) -> int:
+        return flce_workspace_bytes(self.handle, N, H, V, chunk)
+
+    def reserve(self, N, H, V, chunk=0):
+        st = flce_reserve(self.handle, N, H, V, chunk)
+        if st != 0:
+            raise FlceError(st, "flce_reserve")
+
+    def profile_enable(self, enable: bool = True):
+        st = flce_profile_enable(self.handle, enable)
+        if st != 0:
+            raise FlceError(st, "flce_profile_enable")
+
+    def profile_read(self):
+        st, out = flce_profile_read(self.handle)
+        if st != 0:
+            raise FlceError(st, "flce_profile_read")
+        return out
+
+    def check(self, stream=None) -> int:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        return flce_check(self.handle, s.cuda_stream)
+
+    def forward_backward(self, x, W, t, chunk: int = 0, with_lse: bool = False, out=None, stream=None):
+        import torch
+        N, H = x.shape
+        V = W.shape[0]
+        if out is None:
+            loss = torch.empty((), dtype=torch.float32, device=x.device)
+            dx = torch.empty((N, H), dtype=self.dx_dtype, device=x.device)
+            dW = torch.empty((V, H), dtype=self.dw_dtype, device=x.device)
+            lse = torch.empty((N,), dtype=torch.float32, device=x.device) if with_lse else None
+        else:
+            loss, dx, dW, lse = out
+        for name, ten in (("x", x), ("W", W), ("targets", t), ("dx", dx), ("dW", dW)):
+            if not ten.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if x.dtype != self.in_dtype or W.dtype != self.in_dtype or t.dtype != torch.int64:
+            raise ValueError("dtype mismatch with the handle's configuration")
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        st = flce_forward_backward_ex(self.handle, x.data_ptr(), W.data_ptr(), t.data_ptr(), N, H, V,
+                                      chunk, loss.data_ptr(), dx.data_ptr(), dW.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None, s.cuda_stream)
+        if st != 0:
+            raise FlceError(st, "flce_forward_backward")
+        return (loss, dx, dW, lse) if with_lse else (loss, dx, dW)

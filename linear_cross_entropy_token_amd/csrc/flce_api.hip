@@ -1,0 +1,502 @@
+// C-ABI dispatcher of the FLCE library: validation, chunk plan, workspace,
+// and the launch sequence on the caller's stream.
+//
+// The loop is the token-chunk loop of the core-idea section of the "Fused
+// Linear Cross-Entropy" page (42jerrykim.github.io): for each chunk of C
+// tokens, project, turn the logits buffer into dlogits in place, produce dx
+// rows, accumulate dW; the loss and both gradients carry 1/N for the global
+// token count.  Unlike that page's listing, nothing synchronises the host
+// inside the loop: the per-token losses stay on the device and one final
+// kernel reduces them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "flce.h"
+#include "flce_internal.hpp"
+
+namespace {
+
+using flce::In;
+
+constexpr int64_t kTile = flce::kTileM;
+constexpr size_t kAlign = 256;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t N = 0, H = 0, V = 0, C = 0, Vp = 0;
+  int tiles_v = 0, tiles_h = 0;
+  int splits = 1;
+  int64_t k_per_split = 0;
+  size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
+  size_t total = 0;
+};
+
+}  // namespace
+
+namespace {
+
+enum Kernel { K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"logits_lse", "lse_combine", "dlogits", "dx",
+                                           "dx_reduce", "dw", "finalize"};
+
+struct Mark {
+  int kind;                 // Kernel, or -1 for the event that closes a call
+  hipEvent_t ev;
+  double flops, bytes;
+};
+
+struct Stat {
+  int64_t launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+
+}  // namespace
+
+struct flce_handle_s {
+  flce_config_t cfg;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int* flag = nullptr;      // device int, bit 0 = out-of-range target seen
+  bool profiling = false;
+  std::vector<Mark> marks;  // pending events, in stream order
+  std::vector<hipEvent_t> pool;
+  Stat stats[K_COUNT];
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+// Records a profiling event before a launch of `kind` (or kind -1 after the last launch).
+hipError_t mark(flce_handle_s* h, int kind, double flops, double bytes, hipStream_t st) {
+  if (!h->profiling) return hipSuccess;
+  hipEvent_t ev;
+  if (!h->pool.empty()) {
+    ev = h->pool.back();
+    h->pool.pop_back();
+  } else {
+    const hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return e;
+  }
+  h->marks.push_back(Mark{kind, ev, flops, bytes});
+  return hipEventRecord(ev, st);
+}
+
+hipError_t fold_marks(flce_handle_s* h) {
+  hipError_t err = hipSuccess;
+  for (size_t i = 0; i + 1 < h->marks.size(); ++i) {
+    const Mark& m = h->marks[i];
+    if (m.kind < 0) continue;
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(h->marks[i + 1].ev);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, m.ev, h->marks[i + 1].ev);
+    if (e != hipSuccess) {
+      err = e;
+      continue;
+    }
+    Stat& s = h->stats[m.kind];
+    s.launches += 1;
+    s.ms += ms;
+    s.flops += m.flops;
+    s.bytes += m.bytes;
+  }
+  for (const Mark& m : h->marks) h->pool.push_back(m.ev);
+  h->marks.clear();
+  return err;
+}
+
+inline size_t in_size(const flce_config_t& c) { return c.in_dtype == FLCE_BF16 ? 2 : 4; }
+
+bool sizes_ok(int64_t N, int64_t H, int64_t V) {
+  return N >= 1 && H >= 1 && V >= 1;
+}
+
+flce_status_t sizes_supported(int64_t N, int64_t H, int64_t V) {
+  if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 30;
+  if (N > lim || H > lim || V > lim) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
+int64_t next_pow2(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  if (!sizes_ok(N, H, V)) return 0;
+  if (chunk > 0) return std::min(chunk, N);
+  const int64_t inc = cdiv(V, H);
+  int64_t c = next_pow2(cdiv(N, inc));
+  c = std::max<int64_t>(c, 2048);
+  c = std::min<int64_t>(c, 8192);
+  return std::min(c, N);
+}
+
+Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  Plan p;
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.C = effective_chunk(N, H, V, chunk);
+  p.Vp = cdiv(V, kTile) * kTile;
+  p.tiles_v = (int)(p.Vp / kTile);
+  p.tiles_h = (int)cdiv(H, kTile);
+  // dx = G W has only ceil(C/256) x ceil(H/256) output tiles: split the vocabulary
+  // contraction so that about one workgroup per compute unit (256 CUs) runs.
+  const int64_t tiles_dx = cdiv(p.C, kTile) * p.tiles_h;
+  const int64_t bk = 128 / (int64_t)in_size(cfg);
+  int64_t s = std::max<int64_t>(1, 256 / tiles_dx);
+  s = std::min<int64_t>(s, 8);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, p.Vp / (8 * bk)));
+  p.splits = (int)s;
+  p.k_per_split = cdiv(cdiv(p.Vp, s), bk) * bk;
+
+  size_t off = 0;
+  p.off_z = off;    off = align_up(off + (size_t)p.C * p.Vp * in_size(cfg));
+  p.off_pm = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
+  p.off_ps = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
+  p.off_zt = off;   off = align_up(off + (size_t)N * sizeof(float));
+  p.off_lse = off;  off = align_up(off + (size_t)N * sizeof(float));
+  p.off_loss = off; off = align_up(off + (size_t)N * sizeof(float));
+  p.off_part = off;
+  if (p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+flce_status_t ensure_workspace(flce_handle_s* h, size_t need) {
+  if (h->cfg.workspace_limit > 0 && need > (size_t)h->cfg.workspace_limit) return FLCE_ERR_OOM;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  if (h->flag == nullptr) {
+    if (hipMalloc(reinterpret_cast<void**>(&h->flag), sizeof(int)) != hipSuccess) {
+      h->flag = nullptr;
+      (void)hipGetLastError();
+      return FLCE_ERR_OOM;
+    }
+    const int zero = 0;
+    if (hipMemcpy(h->flag, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return FLCE_ERR_HIP;
+  }
+  if (need <= h->ws_bytes) return FLCE_OK;
+  void* p = nullptr;
+  if (hipMalloc(&p, need) != hipSuccess) {
+    (void)hipGetLastError();
+    return FLCE_ERR_OOM;
+  }
+  if (h->ws != nullptr) (void)hipFree(h->ws);
+  h->ws = p;
+  h->ws_bytes = need;
+  return FLCE_OK;
+}
+
+flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V) {
+  (void)cfg;
+  if (!sizes_ok(N, H, V)) return FLCE_ERR_INVALID_ARG;
+  return sizes_supported(N, H, V);
+}
+
+#define FLCE_LAUNCH(call)                         \
+  do {                                            \
+    if ((call) != hipSuccess) return FLCE_ERR_HIP; \
+  } while (0)
+
+flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const void* W,
+                          const int64_t* t, float* loss, void* dx, void* dW, float* lse_out,
+                          hipStream_t st) {
+  const flce_config_t& cfg = h->cfg;
+  const In in = cfg.in_dtype == FLCE_BF16 ? In::BF16 : In::FP32;
+  const size_t es = in_size(cfg);
+  char* ws = static_cast<char*>(h->ws);
+  void* z = ws + p.off_z;
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  float* zt = reinterpret_cast<float*>(ws + p.off_zt);
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
+  float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
+  float* part = reinterpret_cast<float*>(ws + p.off_part);
+  const size_t dx_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
+  const float inv_n = (float)(1.0 / (double)p.N);
+  const double b_in = (double)es, b_dx = (double)dx_es;
+  const double b_dw = cfg.dw_dtype == FLCE_BF16 ? 2.0 : 4.0;
+  const double VH = (double)p.V * (double)p.H;
+
+  for (int64_t s = 0; s < p.N; s += p.C) {
+    const int rows = (int)std::min(p.C, p.N - s);
+    const int tiles_m = (int)cdiv(rows, kTile);
+    const double gemm_flops = 2.0 * rows * VH;
+    const double zbytes = (double)rows * (double)p.V * b_in;
+
+    flce::LogitsArgs la{};
+    la.x = static_cast<const char*>(x) + (size_t)s * p.H * es;
+    la.W = W;
+    la.t = t + s;
+    la.z = z;
+    la.pm = pm;
+    la.ps = ps;
+    la.zt = zt + s;
+    la.ldz = p.Vp;
+    la.pstride = (int)p.C;
+    la.rows = rows;
+    la.H = (int)p.H;
+    la.V = (int)p.V;
+    la.tiles_m = tiles_m;
+    la.tiles_n = p.tiles_v;
+    FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
+    FLCE_LAUNCH(flce::launch_logits(in, la, st));
+
+    flce::CombineArgs ca{};
+    ca.pm = pm;
+    ca.ps = ps;
+    ca.zt = zt + s;
+    ca.t = t + s;
+    ca.lse = lse + s;
+    ca.loss_rows = loss_rows + s;
+    ca.flag = h->flag;
+    ca.pstride = (int)p.C;
+    ca.tiles_n = p.tiles_v;
+    ca.rows = rows;
+    ca.V = (int)p.V;
+    FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
+    FLCE_LAUNCH(flce::launch_combine(ca, st));
+
+    flce::DlogitsArgs ga{};
+    ga.z = z;
+    ga.lse = lse + s;
+    ga.t = t + s;
+    ga.ldz = p.Vp;
+    ga.rows = rows;
+    ga.V = (int)p.V;
+    ga.inv_n = inv_n;
+    FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes, st));
+    FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
+
+    flce::DxArgs xa{};
+    xa.g = z;
+    xa.W = W;
+    xa.part = part;
+    xa.dx = static_cast<char*>(dx) + (size_t)s * p.H * dx_es;
+    xa.ldg = p.Vp;
+    xa.part_stride = p.C * p.H;
+    xa.rows = rows;
+    xa.H = (int)p.H;
+    xa.V = (int)p.V;
+    xa.k_per_split = (int)p.k_per_split;
+    xa.splits = p.splits;
+    xa.tiles_m = tiles_m;
+    xa.tiles_n = p.tiles_h;
+    xa.dx_fp32 = cfg.dx_dtype == FLCE_FP32;
+    FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
+    FLCE_LAUNCH(flce::launch_dx(in, xa, st));
+    if (p.splits > 1) {
+      flce::DxReduceArgs ra{};
+      ra.part = part;
+      ra.dx = xa.dx;
+      ra.part_stride = xa.part_stride;
+      ra.count = (int64_t)rows * p.H;
+      ra.splits = p.splits;
+      ra.dx_fp32 = xa.dx_fp32;
+      FLCE_LAUNCH(mark(h, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
+      FLCE_LAUNCH(flce::launch_dx_reduce(ra, st));
+    }
+
+    flce::DwArgs wa{};
+    wa.g = z;
+    wa.x = la.x;
+    wa.dW = dW;
+    wa.ldg = p.Vp;
+    wa.rows = rows;
+    wa.H = (int)p.H;
+    wa.V = (int)p.V;
+    wa.tiles_m = p.tiles_v;
+    wa.tiles_n = p.tiles_h;
+    wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
+    wa.accumulate = s > 0;
+    FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
+                     zbytes + (double)rows * p.H * b_in + VH * b_dw * (s > 0 ? 2.0 : 1.0), st));
+    FLCE_LAUNCH(flce::launch_dw(in, wa, st));
+  }
+
+  flce::FinalizeArgs fa{};
+  fa.loss_rows = loss_rows;
+  fa.loss = loss;
+  fa.n = p.N;
+  FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
+  FLCE_LAUNCH(flce::launch_finalize(fa, st));
+  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_string(flce_status_t s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_INVALID_ARG: return "FLCE_ERR_INVALID_ARG: invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "FLCE_ERR_UNSUPPORTED: unsupported size, alignment or dtype combination";
+    case FLCE_ERR_OOM: return "FLCE_ERR_OOM: workspace allocation failed or exceeds the configured limit";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP: HIP runtime error";
+    case FLCE_ERR_DATA: return "FLCE_ERR_DATA: a target id was outside [0, V)";
+  }
+  return "unknown flce status";
+}
+
+flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
+  if (cfg == nullptr || out == nullptr) return FLCE_ERR_INVALID_ARG;
+  auto dt_ok = [](int32_t d) { return d == FLCE_BF16 || d == FLCE_FP32; };
+  if (!dt_ok(cfg->in_dtype) || !dt_ok(cfg->dx_dtype) || !dt_ok(cfg->dw_dtype)) return FLCE_ERR_INVALID_ARG;
+  if (cfg->variant != FLCE_CHUNKED && cfg->variant != FLCE_FUSED) return FLCE_ERR_INVALID_ARG;
+  if (cfg->reserved != 0 || cfg->workspace_limit < 0 || cfg->device < 0) return FLCE_ERR_INVALID_ARG;
+  if (cfg->in_dtype == FLCE_FP32 && (cfg->dx_dtype != FLCE_FP32 || cfg->dw_dtype != FLCE_FP32))
+    return FLCE_ERR_UNSUPPORTED;
+  if (cfg->variant == FLCE_FUSED) return FLCE_ERR_UNSUPPORTED;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) {
+    (void)hipGetLastError();
+    return FLCE_ERR_HIP;
+  }
+  flce_handle_s* h = new (std::nothrow) flce_handle_s;
+  if (h == nullptr) return FLCE_ERR_OOM;
+  h->cfg = *cfg;
+  *out = h;
+  return FLCE_OK;
+}
+
+flce_status_t flce_destroy(flce_handle_t h) {
+  if (h == nullptr) return FLCE_OK;
+  {
+    DeviceGuard g(h->cfg.device);
+    (void)fold_marks(h);
+    for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+    if (h->ws != nullptr) (void)hipFree(h->ws);
+    if (h->flag != nullptr) (void)hipFree(h->flag);
+  }
+  delete h;
+  return FLCE_OK;
+}
+
+int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  return effective_chunk(N, H, V, chunk);
+}
+
+size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  if (h == nullptr || validate_sizes(h->cfg, N, H, V) != FLCE_OK) return 0;
+  return make_plan(h->cfg, N, H, V, chunk).total;
+}
+
+flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  if (h == nullptr) return FLCE_ERR_INVALID_ARG;
+  const flce_status_t v = validate_sizes(h->cfg, N, H, V);
+  if (v != FLCE_OK) return v;
+  return ensure_workspace(h, make_plan(h->cfg, N, H, V, chunk).total);
+}
+
+flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,
+                                       const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                       int64_t chunk, float* loss, void* dx, void* dW, float* lse,
+                                       void* stream) {
+  if (h == nullptr || x == nullptr || W == nullptr || targets == nullptr || loss == nullptr ||
+      dx == nullptr || dW == nullptr)
+    return FLCE_ERR_INVALID_ARG;
+  const flce_status_t v = validate_sizes(h->cfg, N, H, V);
+  if (v != FLCE_OK) return v;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(dx) || !aligned16(dW) ||
+      (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return FLCE_ERR_UNSUPPORTED;
+  if (dx == x || dW == W) return FLCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(h->cfg, N, H, V, chunk);
+  const flce_status_t ws = ensure_workspace(h, p.total);
+  if (ws != FLCE_OK) return ws;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  return run_chunked(h, p, x, W, targets, loss, dx, dW, lse, static_cast<hipStream_t>(stream));
+}
+
+flce_status_t flce_forward_backward(flce_handle_t h, const void* x, const void* W,
+                                    const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                    int64_t chunk, float* loss, void* dx, void* dW, void* stream) {
+  return flce_forward_backward_ex(h, x, W, targets, N, H, V, chunk, loss, dx, dW, nullptr, stream);
+}
+
+flce_status_t flce_profile_enable(flce_handle_t h, int enable) {
+  if (h == nullptr) return FLCE_ERR_INVALID_ARG;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  (void)fold_marks(h);
+  for (Stat& s : h->stats) s = Stat{};
+  h->profiling = enable != 0;
+  return FLCE_OK;
+}
+
+flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int capacity, int* count) {
+  if (h == nullptr || count == nullptr || capacity < 0 || (capacity > 0 && out == nullptr))
+    return FLCE_ERR_INVALID_ARG;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  const hipError_t e = fold_marks(h);
+  int n = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    const Stat& s = h->stats[k];
+    if (s.launches == 0) continue;
+    if (n < capacity) {
+      flce_kernel_stat_t& o = out[n];
+      std::memset(&o, 0, sizeof(o));
+      std::strncpy(o.name, kKernelNames[k], sizeof(o.name) - 1);
+      o.launches = s.launches;
+      o.total_ms = s.ms;
+      o.flops = s.flops;
+      o.bytes = s.bytes;
+    }
+    ++n;
+  }
+  *count = n;
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+flce_status_t flce_check(flce_handle_t h, void* stream) {
+  if (h == nullptr) return FLCE_ERR_INVALID_ARG;
+  if (h->flag == nullptr) return FLCE_OK;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int f = 0;
+  if (hipMemcpyAsync(&f, h->flag, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return FLCE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
+  if (f != 0) {
+    const int zero = 0;
+    if (hipMemcpyAsync(h->flag, &zero, sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) return FLCE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
+    return FLCE_ERR_DATA;
+  }
+  return FLCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal interface between the C-ABI dispatcher and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+constexpr int kTileM = 256;   // output tile rows of every GEMM kernel
+constexpr int kTileN = 256;   // output tile columns
+
+// Element type of x and W (and of the chunk's logits/dlogits buffer).
+enum class In { BF16 = 0, FP32 = 1 };
+
+struct LogitsArgs {
+  const void* x;        // chunk's first token row, [rows][H]
+  const void* W;        // [V][H]
+  const int64_t* t;     // chunk's targets [rows]
+  void* z;              // logits buffer [rows][ldz] (in-type), may be null (pass-1 only)
+  float* pm;            // per-(vocab tile, row) max   [tiles_n][pstride]
+  float* ps;            // per-(vocab tile, row) sum of exp(z - max)
+  float* zt;            // target logit per row (fp32 accumulator value) [rows]
+  int64_t ldz;
+  int pstride;
+  int rows, H, V;
+  int tiles_m, tiles_n;
+};
+
+struct CombineArgs {
+  const float* pm;
+  const float* ps;
+  const float* zt;
+  const int64_t* t;
+  float* lse;           // [rows]
+  float* loss_rows;     // [rows]
+  int* flag;            // bit 0: a target outside [0, V)
+  int pstride, tiles_n, rows, V;
+};
+
+struct DlogitsArgs {
+  void* z;              // [rows][ldz] in-type, overwritten with G
+  const float* lse;
+  const int64_t* t;
+  int64_t ldz;
+  int rows, V;
+  float inv_n;
+};
+
+struct DxArgs {
+  const void* g;        // [rows][ldg]
+  const void* W;        // [V][H]
+  float* part;          // [splits][rows_max][H] fp32 when splits > 1
+  void* dx;             // chunk's first row of dx [rows][H]
+  int64_t ldg;
+  int64_t part_stride;  // rows_max * H
+  int rows, H, V;
+  int k_per_split, splits;
+  int tiles_m, tiles_n;
+  int dx_fp32;
+};
+
+struct DxReduceArgs {
+  const float* part;
+  void* dx;
+  int64_t part_stride;
+  int64_t count;        // rows * H
+  int splits;
+  int dx_fp32;
+};
+
+struct DwArgs {
+  const void* g;        // [rows][ldg]
+  const void* x;        // chunk's first token row [rows][H]
+  void* dW;             // [V][H]
+  int64_t ldg;
+  int rows, H, V;
+  int tiles_m, tiles_n;
+  int dw_fp32;
+  int accumulate;       // 0: overwrite dW, 1: dW += G^T x
+};
+
+struct FinalizeArgs {
+  const float* loss_rows;
+  float* loss;
+  int64_t n;
+};
+
+hipError_t launch_logits(In in, const LogitsArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_dlogits(In in, const DlogitsArgs& a, hipStream_t s);
+hipError_t launch_dx(In in, const DxArgs& a, hipStream_t s);
+hipError_t launch_dx_reduce(const DxReduceArgs& a, hipStream_t s);
+hipError_t launch_dw(In in, const DwArgs& a, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+
+}  // namespace flce

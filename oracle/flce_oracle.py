@@ -117,28 +117,22 @@ def flce(x: np.ndarray, W: np.ndarray, t: np.ndarray) -> Dict[str, np.ndarray]:
 
 def flce_rows(x: np.ndarray, W: np.ndarray, t: np.ndarray, rows: Iterable[int],
               n_total: int) -> Dict[str, np.ndarray]:
-    """lse_n, loss_n and dx_n for selected token rows, computed one row at a time.
+    """lse_n, loss_n and dx_n for selected token rows only.
 
-    The same definition as ``flce`` restricted to single rows (a row of dx
-    depends only on that token's logits row), so full-size problems can be
-    checked on sampled rows.
+    The same definition as ``flce`` restricted to the selected rows (a row of
+    dx depends only on that token's logits row), so full-size problems can be
+    checked on sampled rows; ``n_total`` is the N of the whole problem.
     """
     W = np.asarray(W, dtype=np.float64)
-    rows = list(rows)
-    lse = np.empty(len(rows))
-    loss = np.empty(len(rows))
-    dx = np.empty((len(rows), W.shape[1]))
-    for i, n in enumerate(rows):
-        xn = np.asarray(x[n], dtype=np.float64)
-        z = W @ xn
-        m = z.max()
-        lse[i] = m + np.log(np.exp(z - m).sum())
-        loss[i] = lse[i] - z[t[n]]
-        g = np.exp(z - lse[i])
-        g[t[n]] -= 1.0
-        g /= float(n_total)
-        dx[i] = g @ W
-    return {"lse": lse, "loss": loss, "dx": dx}
+    rows = np.asarray(list(rows), dtype=np.int64)
+    xs = np.asarray(x[rows], dtype=np.float64)
+    ts = np.asarray(t, dtype=np.int64)[rows]
+    Z = logits(xs, W)
+    lse = row_logsumexp(Z)
+    loss = row_losses(Z, ts, lse)
+    G = dlogits(Z, ts, lse, n_total)
+    del Z
+    return {"lse": lse, "loss": loss, "dx": G @ W}
 
 
 def logits_bytes(n_tokens: int, vocab: int, bytes_per_elem: int) -> int:

@@ -1,0 +1,192 @@
+"""HIP path vs the CPU oracle (GPU only).
+
+Element-wise comparisons at sizes the oracle finishes in seconds (several
+tiles, ragged chunk and vocabulary tails, edge cases), and at the full
+workload sizes in the benchmark's launch configuration: sampled rows against
+the oracle, exact closed forms (W = 0) and invariants that hold at any size.
+
+Tolerances (written in each assert): loss relative error <= 1e-4; dx and dW
+relative Frobenius error <= 2e-2 for bf16 inputs and <= 1e-5 for fp32 inputs,
+also on the dW rows no target hits (pure softmax part).
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from flce_inputs import make_inputs, WORKLOADS
+from flce_testlib import (require_gpu, run_flce, compare, oracle_full, rel_fro, to_device, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+SMALL = [
+    # id, N, H, V, dtype, chunk, grads dtype
+    ("tiny_fp32_C256", 256, 256, 4096, "fp32", 256, None),
+    ("tiny_fp32_C64", 256, 256, 4096, "fp32", 64, None),
+    ("fp32_ragged", 333, 96, 777, "fp32", 100, None),
+    ("bf16_ragged", 1000, 512, 5000, "bf16", 384, None),
+    ("bf16_ragged_fp32_grads", 1000, 512, 5000, "bf16", 384, "fp32"),
+    ("bf16_N1", 1, 64, 1001, "bf16", 0, None),
+    ("bf16_H64_V1001", 300, 64, 1001, "bf16", 128, None),
+    ("bf16_one_chunk", 512, 256, 3000, "bf16", 0, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_small_vs_oracle(case):
+    name, N, H, V, dt, chunk, gdt = case
+    d = make_inputs(N, H, V, dt, seed=zlib.crc32(name.encode()) % 1000)
+    import torch
+    gd = {"fp32": torch.float32, None: None}[gdt]
+    got = run_flce(d, chunk=chunk, dx_dtype=gd, dw_dtype=gd)
+    want = oracle_full(d)
+    compare(got, want, d["t"], V, TOL[dt], 1e-4, name)
+
+
+def test_tiny_fp32_workload_exact_config():
+    """The tiny fp32 workload as named (N=256, H=256, V=4096, seeded), tolerance 1e-5."""
+    w = WORKLOADS["tiny_fp32"]
+    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
+    got = run_flce(d, chunk=w.chunk, with_lse=True)
+    want = oracle_full(d)
+    compare(got, want, d["t"], w.V, 1e-5, 1e-5, "tiny_fp32")
+    assert np.max(np.abs(got["lse"] - want["lse"])) <= 1e-5 * np.max(np.abs(want["lse"]))
+
+
+@pytest.mark.parametrize("V,zipf", [(128256, False), (151936, True)])
+def test_full_vocab_reduced_tokens(V, zipf):
+    """Full H and V of the Llama-3 / Qwen3 workloads at N=256 (two chunks of 128)."""
+    d = make_inputs(256, 4096, V, "bf16", seed=V, targets="zipf" if zipf else "uniform")
+    got = run_flce(d, chunk=128, with_lse=True)
+    want = oracle_full(d)
+    compare(got, want, d["t"], V, 2e-2, 1e-4, f"V={V}")
+    assert np.max(np.abs(got["lse"] - want["lse"])) <= 1e-4
+
+
+def test_target_extremes_and_collisions():
+    N, H, V = 600, 128, 2000
+    d = make_inputs(N, H, V, "bf16", seed=21)
+    d["t"] = np.where(np.arange(N) % 2 == 0, 0, V - 1).astype(np.int64)
+    compare(run_flce(d, chunk=256), oracle_full(d), d["t"], V, 2e-2, 1e-4, "targets {0,V-1}")
+    d["t"] = np.full(N, 7, dtype=np.int64)
+    compare(run_flce(d, chunk=256), oracle_full(d), d["t"], V, 2e-2, 1e-4, "all targets equal")
+
+
+def test_zero_target_row_isolates_softmax_part():
+    """Append a zero row to W and aim every target at it: the one-hot part of dx is
+    -W[t]/N = 0, so dx is pure softmax and the 2e-2 bound tests that part alone."""
+    N, H, V = 512, 256, 3000
+    d = make_inputs(N, H, V - 1, "bf16", seed=22)
+    d["W"] = np.concatenate([d["W"], np.zeros((1, H), dtype=np.uint16)], axis=0)
+    d["t"] = np.full(N, V - 1, dtype=np.int64)
+    got = run_flce(d, chunk=200)
+    want = oracle_full(d)
+    assert rel_fro(got["dx"], want["dx"]) <= 2e-2
+    compare(got, want, d["t"], V, 2e-2, 1e-4, "zero target row")
+
+
+def test_chunk_invariance_and_determinism():
+    N, H, V = 1024, 256, 4000
+    d = make_inputs(N, H, V, "bf16", seed=23)
+    want = oracle_full(d)
+    outs = []
+    for c in (1024, 384, 100):
+        r = run_flce(d, chunk=c)
+        compare(r, want, d["t"], V, 2e-2, 1e-4, f"chunk={c}")
+        outs.append(r)
+    again = run_flce(d, chunk=384)
+    assert again["loss"] == outs[1]["loss"]
+    assert np.array_equal(again["dx"], outs[1]["dx"]) and np.array_equal(again["dW"], outs[1]["dW"])
+    # the chunk size changes only rounding order (dW accumulation across chunks)
+    assert rel_fro(outs[0]["dW"], outs[2]["dW"]) <= 1e-2
+    assert rel_fro(outs[0]["dx"], outs[2]["dx"]) <= 1e-3
+
+
+def test_out_of_range_target_sets_flag_without_fault():
+    from linear_cross_entropy_token_amd import FusedLinearCrossEntropy
+    N, H, V = 300, 64, 500
+    d = make_inputs(N, H, V, "bf16", seed=24)
+    for bad in (V, -1):
+        d["t"][5] = bad
+        f = FusedLinearCrossEntropy()
+        r = run_flce(d, chunk=128, handle=f)
+        assert math.isnan(r["loss"])
+        assert np.all(np.isfinite(r["dx"])) and np.all(np.isfinite(r["dW"]))
+        assert f.check() == 5          # FLCE_ERR_DATA
+        assert f.check() == 0          # the flag is cleared by the check
+        f.close()
+
+
+def test_reuse_handle_across_shapes():
+    from linear_cross_entropy_token_amd import FusedLinearCrossEntropy
+    f = FusedLinearCrossEntropy()
+    for (N, H, V, c) in ((700, 128, 3000, 256), (200, 64, 900, 0), (900, 256, 5000, 512)):
+        d = make_inputs(N, H, V, "bf16", seed=N)
+        compare(run_flce(d, chunk=c, handle=f), oracle_full(d), d["t"], V, 2e-2, 1e-4, f"{N},{H},{V}")
+    f.close()
+
+
+# ---- full workload sizes, in the benchmark's launch configuration ----------
+
+def _sample_rows(N, C):
+    rows = {0, 1, N - 1, N // 2, C - 1, min(C, N - 1)}
+    rng = np.random.default_rng(N)
+    rows.update(rng.integers(0, N, 10).tolist())
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["llama2_vocab", "llama3_vocab", "qwen3_vocab", "long_context"])
+def test_full_size_sampled(name):
+    w = WORKLOADS[name]
+    print(f"[full-size] {name} N={w.N} H={w.H} V={w.V} chunk={w.chunk}", flush=True)
+    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
+    got = run_flce(d, chunk=w.chunk, with_lse=True)
+    rows = _sample_rows(w.N, w.chunk)
+    W64 = oracle.widen(d["W"], "bf16")
+    want = oracle.flce_rows(oracle.widen(d["x"][rows], "bf16"), W64, d["t"][rows],
+                            range(len(rows)), w.N)
+    assert np.max(np.abs(got["lse"][rows] - want["lse"])) <= 1e-4 * np.max(np.abs(want["lse"]))
+    assert rel_fro(got["dx"][rows], want["dx"]) <= 2e-2
+    # the loss: statistical expectation for these distributions (ln V + 2e-4 H)
+    assert abs(got["loss"] - (math.log(w.V) + 2e-4 * w.H)) < 0.1
+    # invariants at any size: dW column sums vanish; <x,dx> = <W,dW>.  Each column sum of
+    # the softmax part is mean_n x_n (~1/sqrt(N)), so a 1% error in the softmax normalisation
+    # gives |colsum| ~ 1e-2/sqrt(N) ~ 1e-2 |dW column|; bf16 rounding of dW alone gives ~2e-3.
+    dW = got["dW"]
+    colsum = dW.sum(axis=0)
+    assert np.linalg.norm(colsum) <= 1e-2 * np.linalg.norm(dW)
+    x64 = oracle.widen(d["x"], "bf16")
+    a = float(np.sum(x64 * got["dx"]))
+    b = float(np.sum(W64 * dW))
+    assert abs(a - b) <= 1e-2 * max(abs(a), abs(b))
+    got["handle"].close()
+
+
+def test_full_size_zero_weight_closed_form():
+    """W = 0 at the Llama-3-vocabulary size: loss = ln V, dx = 0 and
+    dW[v] = (1/V) mean_n x_n - (1/N) sum_{n: t_n = v} x_n, exactly in the mathematics."""
+    w = WORKLOADS["llama3_vocab"]
+    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
+    d["W"] = np.zeros_like(d["W"])
+    got = run_flce(d, chunk=w.chunk)
+    assert abs(got["loss"] - math.log(w.V)) <= 1e-4 * math.log(w.V)
+    assert np.all(got["dx"] == 0.0)
+    x64 = oracle.widen(d["x"], "bf16")
+    expect = np.empty((w.V, w.H))
+    expect[:] = x64.mean(axis=0) / w.V
+    np.subtract.at(expect, d["t"], x64 / w.N)
+    assert rel_fro(got["dW"], expect) <= 2e-2
+    untargeted = np.ones(w.V, dtype=bool)
+    untargeted[d["t"]] = False
+    assert rel_fro(got["dW"][untargeted], expect[untargeted]) <= 2e-2
+    got["handle"].close()
