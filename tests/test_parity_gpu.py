@@ -147,10 +147,17 @@ def _sample_rows(N, C):
 
 @pytest.mark.parametrize("name", ["llama2_vocab", "llama3_vocab", "qwen3_vocab", "long_context"])
 def test_full_size_sampled(name):
+    """Full workload size, benchmark launch configuration (bf16 outputs): sampled rows of lse
+    and dx against the oracle, and the loss against its expectation.  Then the same launch
+    with fp32 outputs for the exact invariants, which bf16 outputs cannot show: in a targeted
+    vocabulary row the softmax part of dW (~1/(sqrt(N) V)) is below half a bf16 ulp of the
+    one-hot part (~1/N) and rounds away."""
+    import torch
     w = WORKLOADS[name]
     print(f"[full-size] {name} N={w.N} H={w.H} V={w.V} chunk={w.chunk}", flush=True)
     d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
     got = run_flce(d, chunk=w.chunk, with_lse=True)
+    got["handle"].close()
     rows = _sample_rows(w.N, w.chunk)
     W64 = oracle.widen(d["W"], "bf16")
     want = oracle.flce_rows(oracle.widen(d["x"][rows], "bf16"), W64, d["t"][rows],
@@ -159,17 +166,19 @@ def test_full_size_sampled(name):
     assert rel_fro(got["dx"][rows], want["dx"]) <= 2e-2
     # the loss: statistical expectation for these distributions (ln V + 2e-4 H)
     assert abs(got["loss"] - (math.log(w.V) + 2e-4 * w.H)) < 0.1
-    # invariants at any size: dW column sums vanish; <x,dx> = <W,dW>.  Each column sum of
-    # the softmax part is mean_n x_n (~1/sqrt(N)), so a 1% error in the softmax normalisation
-    # gives |colsum| ~ 1e-2/sqrt(N) ~ 1e-2 |dW column|; bf16 rounding of dW alone gives ~2e-3.
-    dW = got["dW"]
-    colsum = dW.sum(axis=0)
-    assert np.linalg.norm(colsum) <= 1e-2 * np.linalg.norm(dW)
+    del got
+    # exact invariants at any size, fp32 outputs: dW column sums vanish; <x,dx> = <W,dW>
+    g32 = run_flce(d, chunk=w.chunk, dx_dtype=torch.float32, dw_dtype=torch.float32)
+    g32["handle"].close()
+    assert rel_fro(g32["dx"][rows], want["dx"]) <= 2e-2
+    dW = g32["dW"]
+    # each column sum of the softmax part is mean_n x_n (~1/sqrt(N)): a 1% error in the
+    # softmax normalisation would give |colsum| ~ 1e-2 |dW column|
+    assert np.linalg.norm(dW.sum(axis=0)) <= 1e-3 * np.linalg.norm(dW)
     x64 = oracle.widen(d["x"], "bf16")
-    a = float(np.sum(x64 * got["dx"]))
+    a = float(np.sum(x64 * g32["dx"]))
     b = float(np.sum(W64 * dW))
-    assert abs(a - b) <= 1e-2 * max(abs(a), abs(b))
-    got["handle"].close()
+    assert abs(a - b) <= 1e-3 * max(abs(a), abs(b))
 
 
 def test_full_size_zero_weight_closed_form():
