@@ -168,7 +168,7 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   // dx = G W has only ceil(C/256) x ceil(H/256) output tiles: split the vocabulary
   // contraction so that about one workgroup per compute unit (256 CUs) runs.
   const int64_t tiles_dx = cdiv(p.C, kTile) * p.tiles_h;
-  const int64_t bk = 128 / (int64_t)in_size(cfg);
+  const int64_t bk = 64 / (int64_t)in_size(cfg);   // contraction elements per k-slice
   int64_t s = std::max<int64_t>(1, 256 / tiles_dx);
   s = std::min<int64_t>(s, 8);
   s = std::min<int64_t>(s, std::max<int64_t>(1, p.Vp / (8 * bk)));
@@ -215,10 +215,18 @@ flce_status_t ensure_workspace(flce_handle_s* h, size_t need) {
   return FLCE_OK;
 }
 
-flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V) {
-  (void)cfg;
+// The kernels address each operand through a 32-bit buffer range: W, one chunk of x and the
+// chunk's logits buffer must each stay below 4 GiB (minus a guard band used for masked lanes).
+flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk) {
   if (!sizes_ok(N, H, V)) return FLCE_ERR_INVALID_ARG;
-  return sizes_supported(N, H, V);
+  const flce_status_t st = sizes_supported(N, H, V);
+  if (st != FLCE_OK) return st;
+  const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
+  const int64_t es = (int64_t)in_size(cfg);
+  const int64_t C = effective_chunk(N, H, V, chunk);
+  const int64_t Vp = cdiv(V, kTile) * kTile;
+  if (V * H * es >= lim || C * H * es >= lim || C * Vp * es >= lim) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
 }
 
 #define FLCE_LAUNCH(call)                         \
@@ -407,13 +415,13 @@ int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk) {
 }
 
 size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
-  if (h == nullptr || validate_sizes(h->cfg, N, H, V) != FLCE_OK) return 0;
+  if (h == nullptr || validate_sizes(h->cfg, N, H, V, chunk) != FLCE_OK) return 0;
   return make_plan(h->cfg, N, H, V, chunk).total;
 }
 
 flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
   if (h == nullptr) return FLCE_ERR_INVALID_ARG;
-  const flce_status_t v = validate_sizes(h->cfg, N, H, V);
+  const flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
   if (v != FLCE_OK) return v;
   return ensure_workspace(h, make_plan(h->cfg, N, H, V, chunk).total);
 }
@@ -425,7 +433,7 @@ flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const voi
   if (h == nullptr || x == nullptr || W == nullptr || targets == nullptr || loss == nullptr ||
       dx == nullptr || dW == nullptr)
     return FLCE_ERR_INVALID_ARG;
-  const flce_status_t v = validate_sizes(h->cfg, N, H, V);
+  const flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
   if (v != FLCE_OK) return v;
   if (!aligned16(x) || !aligned16(W) || !aligned16(dx) || !aligned16(dW) ||
       (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||

@@ -1,25 +1,30 @@
 // Device-side building blocks of the FLCE kernels for gfx950 (MI355X).
 //
 // Every dense contraction of the path (logits = x W^T, dx = G W, dW = G^T x)
-// runs on one MFMA tile engine: a 256-thread workgroup (4 wave64s in a 2x2
-// arrangement) owns a BM x BN output tile, walks the contraction in 128-byte
-// k-slices (64 bf16 or 32 fp32 values) staged through LDS with two buffers,
-// and accumulates in fp32 registers with v_mfma_f32_32x32x16_bf16 (bf16
-// inputs) or v_mfma_f32_32x32x2_f32 (fp32 inputs).
+// runs on one MFMA tile engine:
+//  * a 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
+//    each wave owns 128 x 128 as 4 x 4 blocks of 32 x 32 accumulated in fp32
+//    by v_mfma_f32_32x32x16_bf16 (bf16 inputs) or v_mfma_f32_32x32x2_f32
+//    (fp32 inputs);
+//  * the contraction is walked in k-slices of 64 bytes per operand row
+//    (32 bf16 / 16 fp32) through a 4-stage LDS ring (4 x 32 KiB): operand
+//    tiles are copied HBM -> LDS by buffer_load ... lds (direct-to-LDS DMA,
+//    no VGPR staging), issued three slices ahead of the MFMAs that consume
+//    them; out-of-range rows/columns come back as zeros from the buffer
+//    range check, so ragged edges need no branches;
+//  * an operand stored with the contraction index contiguous ("k-major": x
+//    and W for the logits, G for dx) is kept k-major in LDS and read with
+//    ds_read_b128; an operand whose contraction index is the ROW ("mn-major":
+//    W for dx, G and x for dW) is kept mn-major in LDS and read with the
+//    gfx950 transposing read ds_read_b64_tr_b16, so no operand is ever
+//    transposed in HBM or in registers.
 //
-// LDS holds both operands "k-contiguous": one 128-byte row per output row
-// (A) or column (B), made of eight 16-byte chunks, each chunk holding the
-// consecutive k-values one lane feeds to an MFMA.  Chunk c of row r is
-// stored at chunk position c ^ swz(r), which keeps the 16-byte accesses of
-// every 8-lane group on distinct banks for the MFMA reads and for both
-// loaders' writes.
-//
-// Operands that are stored k-contiguous in HBM (x and W for the logits, G for
-// dx) are copied chunk by chunk.  Operands stored with the contraction index
-// as the *row* (W for dx; G and x for dW) are read as E x E blocks (E rows of
-// one 16-byte chunk, E = 16 / sizeof(T)), transposed in registers and
-// written as E k-contiguous chunks, so every global read stays a coalesced
-// 16-byte load.
+// MFMA roles: the MFMA's A input is the operand that indexes the OUTPUT
+// COLUMNS and its B input the one that indexes the output rows.  Register
+// rg of block (i, j) in lane l then holds
+//   col = 32 i + 8 (rg / 4) + 4 (l / 32) + rg % 4,   row = 32 j + l % 32,
+// so each lane owns runs of 4 consecutive columns of one row: epilogue loads
+// and stores are 8- or 16-byte vectors and row reductions stay in registers.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -27,29 +32,37 @@
 namespace flce {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_t;   // bf16 storage (raw bits)
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;          // one LDS operand row = one k-slice
+constexpr int kTile = 256;             // output tile is kTile x kTile
+constexpr int kStages = 4;             // LDS ring depth
+constexpr int kOpBytes = 16384;        // one operand's part of a stage
+constexpr int kStageBytes = 2 * kOpBytes;
+constexpr int kSmemBytes = kStages * kStageBytes;   // 128 KiB
+constexpr int kSliceBytes = 64;        // bytes of one k-major operand row per slice
+constexpr uint32_t kOOB = 0xFFFFFF00u; // buffer offset beyond every valid range -> zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> { static constexpr int E = 8; };   // values per 16-byte chunk
 template <> struct Elem<float>  { static constexpr int E = 4; };
-
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
-}
+template <typename T> constexpr int slice_k() { return kSliceBytes / (int)sizeof(T); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {   // round to nearest even
   return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return f32_to_bf16(f); }
@@ -61,197 +74,202 @@ template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; 
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
 
-// Butterfly reductions over the 32 lanes of one half-wave (lane bit 5 fixed).
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+// ---------------------------------------------------------------------------
+// Buffer resources and direct-to-LDS copies.
+// ---------------------------------------------------------------------------
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
+    i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
+    int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer over [base, base + bytes): reads at offsets >= bytes return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)(a & 0xffffffffu);
+  r[1] = (int32_t)(uint32_t)((a >> 32) & 0xffffu);
+  r[2] = (int32_t)bytes;
+  r[3] = 0x00020000;
+  return r;
 }
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+
+// Lane l's 16 bytes at buffer offset voff land at lds + 16 l (lds is wave-uniform).
+__device__ __forceinline__ void dma16(i32x4 rsrc, char* lds, uint32_t voff) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)lds, 16,
+                                  (int)voff, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// Global -> register -> LDS loaders for one BMN x (one k-slice) operand tile.
+// LDS layouts (bank-conflict-free for 128- and 256-byte-per-clock banking).
+// k-major: 256 rows x 64 B; 16-byte chunk c of row r sits at chunk c ^ swz_k(r).
+// mn-major (bf16): 32 k-rows x 512 B; 32-byte granule g of row r sits at g ^ swz_mn(r).
+// mn-major (fp32): 16 k-rows x 1 KiB, unswizzled.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_mn(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
 
-// Operand stored [MN][K] with K contiguous (row stride ld elements).
-// Requires k_end % E == 0 (chunk-granular k bound) and 16-byte aligned rows.
-template <typename T, int BMN>
-struct KMajorLoader {
+// One operand: 256 indices along its "mn" dimension by one k-slice per stage.
+// KMAJOR: stored [mn][k] (k contiguous).  Otherwise stored [k][mn] (mn contiguous).
+template <typename T, bool KMAJOR>
+struct Operand {
+  static constexpr bool kKMajor = KMAJOR;
   static constexpr int E = Elem<T>::E;
-  static constexpr int PER = BMN * 8 / kThreads;   // 16-byte chunks per thread
-  u32x4 r[PER];
+  static constexpr int ES = (int)sizeof(T);
+  i32x4 rsrc;
+  uint32_t base[4];     // byte offset of this lane's 16 bytes at k = 0 (kOOB if the mn index is out of range)
+  int kpos[4];          // k offset (within a slice) of this lane's data, for the k bound
+  uint32_t kstride;     // bytes per unit of k
 
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int mn0, int mn_end,
-                                       int k0, int k_end, int tid) {
-    const int c = tid & 7;
-    const int k = k0 + c * E;
-    const bool kok = k < k_end;
+  // ld: row stride (elements); mn_end: valid mn extent; rows beyond the buffer read as zero.
+  __device__ __forceinline__ void init(const T* ptr, int64_t ld, int mn0, int mn_end, uint32_t bytes,
+                                       int wave, int lane) {
+    rsrc = make_rsrc(ptr, bytes);
+    kstride = KMAJOR ? (uint32_t)ES : (uint32_t)(ld * ES);
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int mn = mn0 + (tid >> 3) + 32 * p;
-      if (kok && mn < mn_end) {
-        r[p] = *reinterpret_cast<const u32x4*>(base + (int64_t)mn * ld + k);
+    for (int i = 0; i < 4; ++i) {
+      const int b = wave * 4 + i;                    // 1 KiB block of the 16 KiB operand stage
+      if constexpr (KMAJOR) {
+        const int row = 16 * b + (lane >> 2);
+        const int c = (lane & 3) ^ swz_k(row);
+        const int mn = mn0 + row;
+        base[i] = mn < mn_end ? (uint32_t)(((int64_t)mn * ld + c * E) * ES) : kOOB;
+        kpos[i] = c * E;
+      } else if constexpr (ES == 2) {
+        const int row = 2 * b + (lane >> 5);
+        const int p = lane & 31;
+        const int c = (((p >> 1) ^ swz_mn(row)) << 1) | (p & 1);
+        const int mn = mn0 + c * E;
+        base[i] = mn < mn_end ? (uint32_t)(((int64_t)row * ld + mn) * ES) : kOOB;
+        kpos[i] = row;
       } else {
-        r[p] = u32x4{0u, 0u, 0u, 0u};
+        const int row = b;
+        const int mn = mn0 + lane * E;
+        base[i] = mn < mn_end ? (uint32_t)(((int64_t)row * ld + mn) * ES) : kOOB;
+        kpos[i] = row;
       }
     }
   }
-  __device__ __forceinline__ void store(char* lds, int tid) const {
+
+  // Copies the slice starting at contraction index k0 (k < k_end valid) into lds_op.
+  __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave) const {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int row = (tid >> 3) + 32 * p;
-      *reinterpret_cast<u32x4*>(lds + lds_off(row, tid & 7)) = r[p];
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = base[i] != kOOB && k0 + kpos[i] < k_end;
+      const uint32_t v = ok ? base[i] + (uint32_t)k0 * kstride : kOOB;
+      dma16(rsrc, lds_op + (wave * 4 + i) * 1024, v);
     }
   }
 };
 
-// Operand stored [K][MN] with MN contiguous (row stride ld elements): the
-// contraction index is the row.  Requires mn_end % E == 0; k bound is exact.
-template <typename T, int BMN>
-struct MNMajorLoader {
-  static constexpr int E = Elem<T>::E;
-  static constexpr int MNC = BMN / E;                    // 16-byte chunks across MN
-  static constexpr int PER = 8 * MNC / kThreads;         // E x E blocks per thread
-  static_assert(PER >= 1, "tile too small for the transposing loader");
-  u32x4 r[PER][E];
-
-  __device__ __forceinline__ void load(const T* __restrict__ base, int64_t ld, int mn0, int mn_end,
-                                       int k0, int k_end, int tid) {
+// Fragment of one 32-index block for k-step s (16 bf16 / 8 fp32 k-values) of a slice:
+// lane l supplies index mnb + l % 32 and the k-values 8 (l / 32) .. +7 (bf16) / 4 (l / 32) .. +3 (fp32).
+template <typename T, bool KMAJOR>
+__device__ __forceinline__ u32x4 read_frag(const char* op, int mnb, int s, int lane) {
+  if constexpr (KMAJOR) {
+    const int row = mnb + (lane & 31);
+    const int c = 2 * s + (lane >> 5);
+    return *reinterpret_cast<const u32x4*>(op + row * kSliceBytes + ((c ^ swz_k(row)) << 4));
+  } else if constexpr (sizeof(T) == 2) {
+    const int r = 16 * s + 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int g = (mnb >> 4) + ((lane >> 4) & 1);
+    const int byte = 8 * (lane & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const lds_i16x4* p0 = (const lds_i16x4*)(op + r * 512 + ((g ^ swz_mn(r)) << 5) + byte);
+    const lds_i16x4* p1 = (const lds_i16x4*)(op + (r + 4) * 512 + ((g ^ swz_mn(r + 4)) << 5) + byte);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  } else {
+    const int mn = mnb + (lane & 31);
+    const int k = 8 * s + 4 * (lane >> 5);
+    u32x4 v;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int b = tid + kThreads * q;
-      const int mc = b % MNC;
-      const int kg = b / MNC;
-      const int mn = mn0 + mc * E;
-      const bool mnok = mn < mn_end;
-#pragma unroll
-      for (int rr = 0; rr < E; ++rr) {
-        const int k = k0 + kg * E + rr;
-        if (mnok && k < k_end) {
-          r[q][rr] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + mn);
-        } else {
-          r[q][rr] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(char* lds, int tid) const {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int b = tid + kThreads * q;
-      const int mc = b % MNC;
-      const int kg = b / MNC;
-      if constexpr (E == 8) {
-        // 8x8 transpose of 16-bit values: out[j] holds column j of the block.
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          u32x4 o;
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const uint32_t a = r[q][2 * qd][j >> 1];
-            const uint32_t c = r[q][2 * qd + 1][j >> 1];
-            o[qd] = (j & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-          }
-          *reinterpret_cast<u32x4*>(lds + lds_off(mc * 8 + j, kg)) = o;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 o{r[q][0][j], r[q][1][j], r[q][2][j], r[q][3][j]};
-          *reinterpret_cast<u32x4*>(lds + lds_off(mc * 4 + j, kg)) = o;
-        }
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// MFMA on one LDS stage.  Wave w of the 2x2 arrangement owns rows
-// wm*(BM/2) .. +BM/2 and columns wn*(BN/2) .. +BN/2 as TM x TN blocks of 32x32.
-// Output element (row, col) of block (i, j), register rg of lane l:
-//   row = 32 i + 8 (rg / 4) + 4 (l / 32) + rg % 4,   col = 32 j + l % 32.
-// ---------------------------------------------------------------------------
-template <typename T, int TM, int TN>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[TM][TN], const char* As, const char* Bs,
-                                          int arow0, int brow0, int lane) {
-  const int lr = lane & 31;
-  const int hi = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = 2 * s + hi;
-    u32x4 a[TM], b[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const u32x4*>(As + lds_off(arow0 + 32 * i + lr, c));
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(brow0 + 32 * j + lr, c));
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (Elem<T>::E == 8) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
-                                                              __builtin_bit_cast(bf16x8, b[j]),
-                                                              acc[i][j], 0, 0, 0);
-        } else {
-          const f32x4 af = __builtin_bit_cast(f32x4, a[i]);
-          const f32x4 bf = __builtin_bit_cast(f32x4, b[j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
+    for (int e = 0; e < 4; ++e) v[e] = *reinterpret_cast<const uint32_t*>(op + (k + e) * 1024 + mn * 4);
+    return v;
   }
 }
 
-// Double-buffered main loop over k-slices [k_begin, k_end).
-template <typename T, int BM, int BN, class LA, class LB, class FA, class FB>
-__device__ __forceinline__ void gemm_mainloop(f32x16 (&acc)[BM / 64][BN / 64], char* smem,
-                                              int k_begin, int k_end, FA&& loadA, FB&& loadB) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int BK = kRowBytes / (int)sizeof(T);
-  constexpr int STAGE = (BM + BN) * kRowBytes;
+template <typename T>
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    const f32x4 af = __builtin_bit_cast(f32x4, a);
+    const f32x4 bf = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], c, 0, 0, 0);
+    return c;
+  }
+}
+
+// Waits until at most N of this wave's direct-to-LDS copies are in flight, then
+// joins the workgroup barrier.  One asm statement, so the compiler moves no
+// memory access across it; the plain barrier carries no fence, which would
+// force vmcnt(0) and drain the copies of the later slices.
+template <int N>
+__device__ __forceinline__ void sync_slice() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0, "unsupported vmcnt");
+}
+
+// acc[i][j] += sum over k in [k_begin, k_end) of C[col 32i + ..][k] * R[row 32j + ..][k] for the
+// wave's 128 x 128 part of the tile.  Col and Row fill their halves of each LDS stage.
+template <typename T, class OpC, class OpR>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const OpC& C, const OpR& R,
+                                          int k_begin, int k_end) {
+  constexpr int BK = slice_k<T>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int arow0 = (wave >> 1) * (BM / 2);
-  const int brow0 = (wave & 1) * (BN / 2);
+  const int rowb = (wave >> 1) * 128;
+  const int colb = (wave & 1) * 128;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  LA la;
-  LB lb;
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  if (nk <= 0) return;
-  loadA(la, k_begin);
-  loadB(lb, k_begin);
-  la.store(smem, tid);
-  lb.store(smem + BM * kRowBytes, tid);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE;
-    char* nxt = smem + ((kt + 1) & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      loadA(la, k_begin + (kt + 1) * BK);
-      loadB(lb, k_begin + (kt + 1) * BK);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (s < nk) {
+      char* st = smem + s * kStageBytes;
+      C.issue(st, k_begin + s * BK, k_end, wave);
+      R.issue(st + kOpBytes, k_begin + s * BK, k_end, wave);
     }
-    mma_stage<T, TM, TN>(acc, cur, cur + BM * kRowBytes, arow0, brow0, lane);
-    if (more) {
-      la.store(nxt, tid);
-      lb.store(nxt + BM * kRowBytes, tid);
-    }
-    __syncthreads();
   }
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's copies of slice kt have landed once at most the later slices' 8 copies each remain
+    // (then every wave's copies of slice kt are visible and slice kt-1 is consumed)
+    const int later = min(kStages - 2, nk - 1 - kt);
+    if (later >= 2) sync_slice<16>();
+    else if (later == 1) sync_slice<8>();
+    else sync_slice<0>();
+    if (kt + kStages - 1 < nk) {
+      char* st = smem + ((kt + kStages - 1) % kStages) * kStageBytes;
+      const int k0 = k_begin + (kt + kStages - 1) * BK;
+      C.issue(st, k0, k_end, wave);
+      R.issue(st + kOpBytes, k0, k_end, wave);
+    }
+    const char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = read_frag<T, OpR::kKMajor>(st + kOpBytes, rowb + 32 * j, s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(a[i], b[j], acc[i][j]);
+    }
+  }
+  __syncthreads();   // LDS free for the epilogue
 }
 
 // Maps the hardware workgroup index to a logical tile index so that each of

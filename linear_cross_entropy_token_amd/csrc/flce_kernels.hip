@@ -3,10 +3,10 @@
 // Per token chunk (the four steps of the core idea of the "Fused Linear
 // Cross-Entropy" page, 42jerrykim.github.io):
 //   logits_lse   z = x_c W^T on MFMA; the epilogue reduces each row of the
-//                256-wide vocabulary tile to (max, sum exp(z - max)) with
-//                half-wave butterflies, picks up the target logit, and stores
-//                z into the chunk buffer (online-softmax statistics as on the
-//                "Unsloth deep architecture" page, streaming CE kernel).
+//                256-wide vocabulary tile to (max, sum exp(z - max)) in
+//                registers, picks up the target logit, and stores z into the
+//                chunk buffer (online-softmax statistics as on the "Unsloth
+//                deep architecture" page, streaming CE kernel).
 //   lse_combine  lse_n = M + ln sum_j s_j e^(m_j - M) over the vocab tiles,
 //                per-row loss lse_n - z[n, t_n].
 //   dlogits      G = (exp(z - lse) - onehot(t)) / N written over z
@@ -19,12 +19,23 @@
 
 namespace flce {
 
-constexpr int BM = kTileM;
-constexpr int BN = kTileN;
-constexpr int kSmemBytes = 2 * (BM + BN) * kRowBytes;   // 128 KiB: two k-slice stages
+static_assert(kTile == kTileM && kTile == kTileN, "tile sizes of the dispatcher and the engine differ");
+
+// Output coordinates of accumulator (i, j, q) in this lane: the 4 consecutive
+// columns col0 .. col0 + 3 of one row (see the engine header).
+struct Frag {
+  int rowb, colb, lane;
+  __device__ __forceinline__ int row(int j) const { return rowb + 32 * j + (lane & 31); }
+  __device__ __forceinline__ int col0(int i, int q) const { return colb + 32 * i + 8 * q + 4 * (lane >> 5); }
+};
+__device__ __forceinline__ Frag frag_coords() {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  return Frag{(wave >> 1) * 128, (wave & 1) * 128, tid & 63};
+}
 
 // ---------------------------------------------------------------------------
-// logits + LSE partials + target gather (+ z store)
+// logits + LSE partials + target gather + z store
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
@@ -33,74 +44,84 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
   const int tm = L % a.tiles_m;
   const int tn = L / a.tiles_m;
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
-  const T* X = static_cast<const T*>(a.x);
-  const T* W = static_cast<const T*>(a.W);
+  const int m0 = tm * kTile;   // tokens
+  const int n0 = tn * kTile;   // vocabulary ids
+  constexpr int ES = (int)sizeof(T);
 
-  f32x16 acc[BM / 64][BN / 64];
-  gemm_mainloop<T, BM, BN, KMajorLoader<T, BM>, KMajorLoader<T, BN>>(
-      acc, smem, 0, a.H,
-      [&](KMajorLoader<T, BM>& l, int k0) { l.load(X, a.H, m0, a.rows, k0, a.H, tid); },
-      [&](KMajorLoader<T, BN>& l, int k0) { l.load(W, a.H, n0, a.V, k0, a.H, tid); });
+  Operand<T, true> C, R;      // columns: W rows (vocab), rows: x rows (tokens)
+  C.init(static_cast<const T*>(a.W), a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
+  R.init(static_cast<const T*>(a.x), a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6,
+         tid & 63);
+  f32x16 acc[4][4];
+  gemm_tile<T>(acc, smem, C, R, 0, a.H);
 
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  float* red = reinterpret_cast<float*>(smem);                 // [4][BM]: max wn0, max wn1, sum wn0, sum wn1
-  int* trel = reinterpret_cast<int*>(smem + 4 * BM * sizeof(float));
-  if (tid < BM) {
+  const Frag f = frag_coords();
+  float* red = reinterpret_cast<float*>(smem);                 // [4][kTile]: max wc0, max wc1, sum wc0, sum wc1
+  int* trel = reinterpret_cast<int*>(smem + 4 * kTile * sizeof(float));
+  {
     const int r = m0 + tid;
     int rel = -1;
     if (r < a.rows) {
       const int64_t d = a.t[r] - (int64_t)n0;
-      rel = (d >= 0 && d < BN) ? (int)d : -1;
+      rel = (d >= 0 && d < kTile) ? (int)d : -1;
     }
     trel[tid] = rel;
   }
   __syncthreads();
 
   const float ninf = -__builtin_inff();
+  const int wc = (tid >> 6) & 1;
+  const int vlim = a.V - n0;                // columns >= vlim are padding
   T* Z = static_cast<T*>(a.z);
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i) {
+  for (int j = 0; j < 4; ++j) {
+    const int row = f.row(j);
+    const int grow = m0 + row;
+    float mx = ninf;
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int row = wm * (BM / 2) + 32 * i + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
-      const int grow = m0 + row;
-      float mx = ninf;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < BN / 64; ++j) {
-        const int col = wn * (BN / 2) + 32 * j + (lane & 31);
-        if (n0 + col < a.V) mx = fmaxf(mx, acc[i][j][rg]);
-      }
-      mx = half_max(mx);
-      float s = 0.f;
+      for (int rg = 0; rg < 16; ++rg)
+        if (f.col0(i, rg >> 2) + (rg & 3) < vlim) mx = fmaxf(mx, acc[i][j][rg]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < BN / 64; ++j) {
-        const int col = wn * (BN / 2) + 32 * j + (lane & 31);
-        if (n0 + col < a.V) s += fast_exp(acc[i][j][rg] - mx);
-      }
-      s = half_sum(s);
-      if ((lane & 31) == 0) {
-        red[wn * BM + row] = mx;
-        red[(2 + wn) * BM + row] = s;
-      }
-      if (grow < a.rows) {
-        const int tr = trel[row];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < BN / 64; ++j) {
-          const int col = wn * (BN / 2) + 32 * j + (lane & 31);
-          if (col == tr) a.zt[grow] = acc[i][j][rg];
-          if (Z != nullptr && n0 + col < a.V) Z[(int64_t)grow * a.ldz + n0 + col] = from_f32<T>(acc[i][j][rg]);
+      for (int rg = 0; rg < 16; ++rg)
+        if (f.col0(i, rg >> 2) + (rg & 3) < vlim) s += fast_exp(acc[i][j][rg] - mx);
+    s += __shfl_xor(s, 32, 64);
+    if (f.lane < 32) {
+      red[wc * kTile + row] = mx;
+      red[(2 + wc) * kTile + row] = s;
+    }
+    if (grow < a.rows) {
+      const int tr = trel[row];
+      T* zrow = Z + (int64_t)grow * a.ldz + n0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = f.col0(i, q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c0 + e == tr) a.zt[grow] = acc[i][j][4 * q + e];
+          if constexpr (ES == 2) {
+            u32x2 v{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                    pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            *reinterpret_cast<u32x2*>(zrow + c0) = v;
+          } else {
+            f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(zrow + c0) = v;
+          }
         }
       }
     }
   }
   __syncthreads();
-  if (tid < BM && m0 + tid < a.rows) {
-    const float M0 = red[tid], M1 = red[BM + tid];
-    const float S0 = red[2 * BM + tid], S1 = red[3 * BM + tid];
+  if (m0 + tid < a.rows) {
+    const float M0 = red[tid], M1 = red[kTile + tid];
+    const float S0 = red[2 * kTile + tid], S1 = red[3 * kTile + tid];
     const float M = fmaxf(M0, M1);
     const float S = (M0 == ninf ? 0.f : S0 * fast_exp(M0 - M)) + (M1 == ninf ? 0.f : S1 * fast_exp(M1 - M));
     a.pm[(int64_t)tn * a.pstride + m0 + tid] = M;
@@ -109,20 +130,39 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// per-row combine of the vocabulary-tile partials
+// per-row combine of the vocabulary-tile partials: 32 rows per block, 8 lanes
+// per row each folding every 8th tile, then a fold of the 8 partial results
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.rows) return;
+  __shared__ float sm[8][32], ss[8][32];
+  const int rl = threadIdx.x & 31;
+  const int part = threadIdx.x >> 5;
+  const int r = blockIdx.x * 32 + rl;
   const float ninf = -__builtin_inff();
-  float M = ninf;
-  for (int j = 0; j < a.tiles_n; ++j) M = fmaxf(M, a.pm[(int64_t)j * a.pstride + r]);
-  float S = 0.f;
-  for (int j = 0; j < a.tiles_n; ++j) {
-    const float m = a.pm[(int64_t)j * a.pstride + r];
-    if (m != ninf) S += a.ps[(int64_t)j * a.pstride + r] * fast_exp(m - M);
+  float M = ninf, S = 0.f;
+  if (r < a.rows) {
+    for (int j = part; j < a.tiles_n; j += 8) {
+      const float m = a.pm[(int64_t)j * a.pstride + r];
+      const float s = a.ps[(int64_t)j * a.pstride + r];
+      if (m == ninf) continue;
+      if (m > M) {
+        S = S * fast_exp(M - m) + s;
+        M = m;
+      } else {
+        S += s * fast_exp(m - M);
+      }
+    }
   }
-  const float lse = M + fast_log(S);
+  sm[part][rl] = M;
+  ss[part][rl] = S;
+  __syncthreads();
+  if (part != 0 || r >= a.rows) return;
+  float MM = ninf;
+  for (int p = 0; p < 8; ++p) MM = fmaxf(MM, sm[p][rl]);
+  float SS = 0.f;
+  for (int p = 0; p < 8; ++p)
+    if (sm[p][rl] != ninf) SS += ss[p][rl] * fast_exp(sm[p][rl] - MM);
+  const float lse = MM + fast_log(SS);
   const int64_t tv = a.t[r];
   const bool ok = tv >= 0 && tv < a.V;
   a.lse[r] = lse;
@@ -176,43 +216,42 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   const int rem = L - split * tiles;
   const int tn = rem % a.tiles_n;
   const int tm = rem / a.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * kTile, n0 = tn * kTile;   // tokens, hidden units
   const int ks = split * a.k_per_split;
-  const int ke = min((int64_t)ks + a.k_per_split, a.ldg);
-  const int kw = min(ke, a.V);
-  const T* G = static_cast<const T*>(a.g);
-  const T* W = static_cast<const T*>(a.W);
+  const int ke = (int)min((int64_t)ks + a.k_per_split, a.ldg);
+  constexpr int ES = (int)sizeof(T);
 
-  f32x16 acc[BM / 64][BN / 64];
-  gemm_mainloop<T, BM, BN, KMajorLoader<T, BM>, MNMajorLoader<T, BN>>(
-      acc, smem, ks, ke,
-      [&](KMajorLoader<T, BM>& l, int k0) { l.load(G, a.ldg, m0, a.rows, k0, ke, tid); },
-      [&](MNMajorLoader<T, BN>& l, int k0) { l.load(W, a.H, n0, a.H, k0, kw, tid); });
+  Operand<T, false> C;   // columns: W as [v][h] (hidden contiguous)
+  Operand<T, true> R;    // rows: G as [token][v]
+  C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
+  R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES), tid >> 6,
+         tid & 63);
+  f32x16 acc[4][4];
+  gemm_tile<T>(acc, smem, C, R, ks, ke);
 
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const Frag f = frag_coords();
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int grow = m0 + f.row(j);
+    if (grow >= a.rows) continue;
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int grow = m0 + wm * (BM / 2) + 32 * i + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
-      if (grow >= a.rows) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < BN / 64; ++j) {
-        const int col = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + f.col0(i, q);
         if (col >= a.H) continue;
-        const float v = acc[i][j][rg];
+        const f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         const int64_t o = (int64_t)grow * a.H + col;
         if (a.splits > 1) {
-          a.part[split * a.part_stride + o] = v;
+          *reinterpret_cast<f32x4*>(a.part + split * a.part_stride + o) = v;
         } else if (a.dx_fp32) {
-          static_cast<float*>(a.dx)[o] = v;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + o) = v;
         } else {
-          static_cast<bf16_t*>(a.dx)[o] = f32_to_bf16(v);
+          *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + o) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
       }
-    }
+  }
 }
 
 __global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
@@ -223,11 +262,8 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
     if (a.dx_fp32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + i) = s;
     } else {
-      bf16_t* o = static_cast<bf16_t*>(a.dx) + i;
-      uint32_t lo = f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
-      uint32_t hi = f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
-      reinterpret_cast<uint32_t*>(o)[0] = lo;
-      reinterpret_cast<uint32_t*>(o)[1] = hi;
+      *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + i) =
+          u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     }
   }
 }
@@ -242,42 +278,47 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
   const int tn = L % a.tiles_n;
   const int tm = L / a.tiles_n;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const T* G = static_cast<const T*>(a.g);
-  const T* X = static_cast<const T*>(a.x);
+  const int m0 = tm * kTile, n0 = tn * kTile;   // vocabulary ids, hidden units
+  constexpr int ES = (int)sizeof(T);
 
-  f32x16 acc[BM / 64][BN / 64];
-  gemm_mainloop<T, BM, BN, MNMajorLoader<T, BM>, MNMajorLoader<T, BN>>(
-      acc, smem, 0, a.rows,
-      [&](MNMajorLoader<T, BM>& l, int k0) { l.load(G, a.ldg, m0, (int)a.ldg, k0, a.rows, tid); },
-      [&](MNMajorLoader<T, BN>& l, int k0) { l.load(X, a.H, n0, a.H, k0, a.rows, tid); });
+  Operand<T, false> C;   // columns: x_c as [token][h]
+  Operand<T, false> R;   // rows: G as [token][v]
+  C.init(static_cast<const T*>(a.x), a.H, n0, a.H, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6, tid & 63);
+  R.init(static_cast<const T*>(a.g), a.ldg, m0, (int)a.ldg, (uint32_t)((int64_t)a.rows * a.ldg * ES),
+         tid >> 6, tid & 63);
+  f32x16 acc[4][4];
+  gemm_tile<T>(acc, smem, C, R, 0, a.rows);
 
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const Frag f = frag_coords();
 #pragma unroll
-  for (int i = 0; i < BM / 64; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int v = m0 + f.row(j);
+    if (v >= a.V) continue;
 #pragma unroll
-    for (int rg = 0; rg < 16; ++rg) {
-      const int v = m0 + wm * (BM / 2) + 32 * i + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
-      if (v >= a.V) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < BN / 64; ++j) {
-        const int h = n0 + wn * (BN / 2) + 32 * j + (lane & 31);
+      for (int q = 0; q < 4; ++q) {
+        const int h = n0 + f.col0(i, q);
         if (h >= a.H) continue;
+        f32x4 val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         const int64_t o = (int64_t)v * a.H + h;
-        float val = acc[i][j][rg];
         if (a.dw_fp32) {
-          float* p = static_cast<float*>(a.dW) + o;
+          f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.dW) + o);
           if (a.accumulate) val += *p;
           *p = val;
         } else {
-          bf16_t* p = static_cast<bf16_t*>(a.dW) + o;
-          if (a.accumulate) val += bf16_to_f32(*p);
-          *p = f32_to_bf16(val);
+          u32x2* p = reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dW) + o);
+          if (a.accumulate) {
+            const u32x2 old = *p;
+            val[0] += bf16_to_f32(old[0] & 0xffffu);
+            val[1] += bf16_to_f32(old[0] >> 16);
+            val[2] += bf16_to_f32(old[1] & 0xffffu);
+            val[3] += bf16_to_f32(old[1] >> 16);
+          }
+          *p = u32x2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
         }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -314,7 +355,7 @@ hipError_t launch_logits(In in, const LogitsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(lse_combine_kernel, dim3((a.rows + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((a.rows + 31) / 32), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
