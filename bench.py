@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="also measure the peak HBM of the materialised-logits PyTorch path")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="after the run, copy a buffer of this many GiB once (a plain copy kernel of "
+                         "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -218,6 +221,16 @@ def main():
         f.close()
         del dx, dW
         extra["materialised_baseline"] = materialised_peak(x, W, t)
+
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = n * 4
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

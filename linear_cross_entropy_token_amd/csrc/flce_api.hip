@@ -168,7 +168,7 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   // dx = G W has only ceil(C/256) x ceil(H/256) output tiles: split the vocabulary
   // contraction so that about one workgroup per compute unit (256 CUs) runs.
   const int64_t tiles_dx = cdiv(p.C, kTile) * p.tiles_h;
-  const int64_t bk = 64 / (int64_t)in_size(cfg);   // contraction elements per k-slice
+  const int64_t bk = flce::kSliceBytesABI / (int64_t)in_size(cfg);   // contraction elements per k-slice
   int64_t s = std::max<int64_t>(1, 256 / tiles_dx);
   s = std::min<int64_t>(s, 8);
   s = std::min<int64_t>(s, std::max<int64_t>(1, p.Vp / (8 * bk)));

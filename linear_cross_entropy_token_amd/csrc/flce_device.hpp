@@ -6,12 +6,14 @@
 //    each wave owns 128 x 128 as 4 x 4 blocks of 32 x 32 accumulated in fp32
 //    by v_mfma_f32_32x32x16_bf16 (bf16 inputs) or v_mfma_f32_32x32x2_f32
 //    (fp32 inputs);
-//  * the contraction is walked in k-slices of 64 bytes per operand row
-//    (32 bf16 / 16 fp32) through a 4-stage LDS ring (4 x 32 KiB): operand
-//    tiles are copied HBM -> LDS by buffer_load ... lds (direct-to-LDS DMA,
-//    no VGPR staging), issued three slices ahead of the MFMAs that consume
-//    them; out-of-range rows/columns come back as zeros from the buffer
-//    range check, so ragged edges need no branches;
+//  * the contraction is walked in k-slices of 128 bytes per operand row
+//    (64 bf16 / 32 fp32, one full cache line per k-major row) through a
+//    2-stage LDS ring (2 x 64 KiB): operand tiles are copied HBM -> LDS by
+//    buffer_load ... lds (direct-to-LDS DMA, no VGPR staging), issued one
+//    slice ahead of the MFMAs that consume them; out-of-range rows/columns
+//    come back as zeros from the buffer range check, so ragged edges need no
+//    branches.  (Measured on MI355X: full-line requests with 2 stages beat
+//    half-line requests with 4 stages of 32 KiB on all three GEMMs.)
 //  * an operand stored with the contraction index contiguous ("k-major": x
 //    and W for the logits, G for dx) is kept k-major in LDS and read with
 //    ds_read_b128; an operand whose contraction index is the ROW ("mn-major":
@@ -29,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "flce_internal.hpp"
+
 namespace flce {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -43,11 +47,13 @@ typedef uint16_t bf16_t;   // bf16 storage (raw bits)
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;             // output tile is kTile x kTile
-constexpr int kStages = 4;             // LDS ring depth
-constexpr int kOpBytes = 16384;        // one operand's part of a stage
+constexpr int kStages = 2;                          // LDS ring depth
+constexpr int kSliceBytes = kSliceBytesABI;         // bytes of one k-major operand row per slice
+constexpr int kOpBytes = kTile * kSliceBytes;       // one operand's part of a stage (32 KiB)
 constexpr int kStageBytes = 2 * kOpBytes;
 constexpr int kSmemBytes = kStages * kStageBytes;   // 128 KiB
-constexpr int kSliceBytes = 64;        // bytes of one k-major operand row per slice
+constexpr int kBlocksPerWave = kOpBytes / 1024 / 4; // 1 KiB DMA blocks per wave per operand and slice
+constexpr int kSteps = kSliceBytes / 32;            // MFMA k-steps per slice
 constexpr uint32_t kOOB = 0xFFFFFF00u; // buffer offset beyond every valid range -> zeros
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -100,11 +106,11 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, char* lds, uint32_t voff) {
 
 // ---------------------------------------------------------------------------
 // LDS layouts (bank-conflict-free for 128- and 256-byte-per-clock banking).
-// k-major: 256 rows x 64 B; 16-byte chunk c of row r sits at chunk c ^ swz_k(r).
-// mn-major (bf16): 32 k-rows x 512 B; 32-byte granule g of row r sits at g ^ swz_mn(r).
-// mn-major (fp32): 16 k-rows x 1 KiB, unswizzled.
+// k-major: 256 rows x 128 B; 16-byte chunk c of row r sits at chunk c ^ swz_k(r).
+// mn-major (bf16): 64 k-rows x 512 B; 32-byte granule g of row r sits at g ^ swz_mn(r).
+// mn-major (fp32): 32 k-rows x 1 KiB, unswizzled.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 __device__ __forceinline__ int swz_mn(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
 
 // One operand: 256 indices along its "mn" dimension by one k-slice per stage.
@@ -115,8 +121,8 @@ struct Operand {
   static constexpr int E = Elem<T>::E;
   static constexpr int ES = (int)sizeof(T);
   i32x4 rsrc;
-  uint32_t base[4];     // byte offset of this lane's 16 bytes at k = 0 (kOOB if the mn index is out of range)
-  int kpos[4];          // k offset (within a slice) of this lane's data, for the k bound
+  uint32_t base[kBlocksPerWave];  // byte offset of this lane's 16 bytes at k = 0 (kOOB if mn is out of range)
+  int kpos[kBlocksPerWave];       // k offset (within a slice) of this lane's data, for the k bound
   uint32_t kstride;     // bytes per unit of k
 
   // ld: row stride (elements); mn_end: valid mn extent; rows beyond the buffer read as zero.
@@ -125,11 +131,11 @@ struct Operand {
     rsrc = make_rsrc(ptr, bytes);
     kstride = KMAJOR ? (uint32_t)ES : (uint32_t)(ld * ES);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = wave * 4 + i;                    // 1 KiB block of the 16 KiB operand stage
+    for (int i = 0; i < kBlocksPerWave; ++i) {
+      const int b = wave * kBlocksPerWave + i;       // 1 KiB block of the operand's stage
       if constexpr (KMAJOR) {
-        const int row = 16 * b + (lane >> 2);
-        const int c = (lane & 3) ^ swz_k(row);
+        const int row = 8 * b + (lane >> 3);
+        const int c = (lane & 7) ^ swz_k(row);
         const int mn = mn0 + row;
         base[i] = mn < mn_end ? (uint32_t)(((int64_t)mn * ld + c * E) * ES) : kOOB;
         kpos[i] = c * E;
@@ -152,15 +158,15 @@ struct Operand {
   // Copies the slice starting at contraction index k0 (k < k_end valid) into lds_op.
   __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kBlocksPerWave; ++i) {
       const bool ok = base[i] != kOOB && k0 + kpos[i] < k_end;
       const uint32_t v = ok ? base[i] + (uint32_t)k0 * kstride : kOOB;
-      dma16(rsrc, lds_op + (wave * 4 + i) * 1024, v);
+      dma16(rsrc, lds_op + (wave * kBlocksPerWave + i) * 1024, v);
     }
   }
 };
 
-// Fragment of one 32-index block for k-step s (16 bf16 / 8 fp32 k-values) of a slice:
+// Fragment of one 32-index block for k-step s (16 bf16 / 8 fp32 k-values; kSteps per slice):
 // lane l supplies index mnb + l % 32 and the k-values 8 (l / 32) .. +7 (bf16) / 4 (l / 32) .. +3 (fp32).
 template <typename T, bool KMAJOR>
 __device__ __forceinline__ u32x4 read_frag(const char* op, int mnb, int s, int lane) {
@@ -211,8 +217,8 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 template <int N>
 __device__ __forceinline__ void sync_slice() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "unsupported vmcnt");
 }
 
@@ -243,11 +249,12 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const
     }
   }
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's copies of slice kt have landed once at most the later slices' 8 copies each remain
+    // this wave's copies of slice kt have landed once at most the later slices' copies remain
     // (then every wave's copies of slice kt are visible and slice kt-1 is consumed)
+    constexpr int kPer = 2 * kBlocksPerWave;   // copies per wave per slice
     const int later = min(kStages - 2, nk - 1 - kt);
-    if (later >= 2) sync_slice<16>();
-    else if (later == 1) sync_slice<8>();
+    if (later >= 2) sync_slice<2 * kPer>();
+    else if (later == 1) sync_slice<kPer>();
     else sync_slice<0>();
     if (kt + kStages - 1 < nk) {
       char* st = smem + ((kt + kStages - 1) % kStages) * kStageBytes;
@@ -257,7 +264,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const
     }
     const char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
       u32x4 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) a[i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);

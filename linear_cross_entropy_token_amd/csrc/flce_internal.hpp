@@ -5,8 +5,9 @@
 
 namespace flce {
 
-constexpr int kTileM = 256;   // output tile rows of every GEMM kernel
-constexpr int kTileN = 256;   // output tile columns
+constexpr int kTileM = 256;        // output tile rows of every GEMM kernel
+constexpr int kTileN = 256;        // output tile columns
+constexpr int kSliceBytesABI = 128; // bytes of contraction per operand row and k-slice (split-K granule)
 
 // Element type of x and W (and of the chunk's logits/dlogits buffer).
 enum class In { BF16 = 0, FP32 = 1 };
