@@ -52,9 +52,9 @@ WORKLOADS: Dict[str, Workload] = {
                           "tiny FLCE, fp32, N=256 H=256 V=4096"),
     "llama2_vocab": Workload("llama2_vocab", 8192, 4096, 32000, "bf16", "uniform", 2048, 2,
                              "Llama-2 vocab, bf16, N=8192 (2x4096) H=4096 V=32000, C=2048"),
-    "llama3_vocab": Workload("llama3_vocab", 16384, 4096, 128256, "bf16", "uniform", 2048, 3,
+    "llama3_vocab": Workload("llama3_vocab", 16384, 4096, 128256, "bf16", "uniform", 4096, 3,
                              "Llama-3 vocab, bf16, N=16384 (1x16384) H=4096 V=128256"),
-    "qwen3_vocab": Workload("qwen3_vocab", 16384, 4096, 151936, "bf16", "zipf", 2048, 4,
+    "qwen3_vocab": Workload("qwen3_vocab", 16384, 4096, 151936, "bf16", "zipf", 4096, 4,
                             "Qwen3 vocab, bf16, N=16384 (4x4096) H=4096 V=151936, Zipf(1.1) targets"),
     "long_context": Workload("long_context", 131072, 4096, 128256, "bf16", "uniform", 4096, 5,
                              "long context, bf16, N=131072 (1x128K) H=4096 V=128256"),

@@ -99,10 +99,11 @@ flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const voi
                                        int64_t chunk, float* loss, void* dx, void* dW, float* lse,
                                        void* stream);
 
-/* Token chunk the call would use: chunk clamped to [1, N] when positive; for chunk <= 0 the
- * size rule of the FLCE page's trade-offs section, next_pow2(ceil(N / ceil(V/H))), raised to at
- * least 2048 tokens (below that the per-chunk re-read of W makes the path HBM-bound on MI355X)
- * and at most 8192, then clamped to N.  Returns 0 for invalid sizes. */
+/* Token chunk the call would use (for bf16 inputs): chunk clamped to [1, N] when positive; for
+ * chunk <= 0 the size rule of the FLCE page's trade-offs section, next_pow2(ceil(N / ceil(V/H))),
+ * raised to at least 4096 tokens (on MI355X the chunk's GEMMs run faster with the longer token
+ * contraction, and below ~2048 the per-chunk re-read of W dominates), capped at 8192 and so that
+ * the chunk's logits buffer stays within 1.5 GB, then clamped to N.  Returns 0 for invalid sizes. */
 int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk);
 
 /* Workspace bytes a call with these sizes needs (0 for invalid sizes). */

@@ -146,13 +146,20 @@ int64_t next_pow2(int64_t v) {
   return p;
 }
 
-int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk) {
+// Automatic chunk: the size rule of the FLCE page's trade-offs section (next power of two of
+// N / ceil(V / H)), raised to 4096 tokens: on MI355X the per-chunk GEMMs run faster with the
+// longer token contraction (dW) and the larger output (dx needs no split at 4096 x 4096), and
+// below ~2048 tokens the per-chunk re-read of W dominates.  Capped at 8192 and so that the
+// chunk's bf16/fp32 logits buffer stays within 1.5 GB.
+int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t es) {
   if (!sizes_ok(N, H, V)) return 0;
   if (chunk > 0) return std::min(chunk, N);
   const int64_t inc = cdiv(V, H);
   int64_t c = next_pow2(cdiv(N, inc));
-  c = std::max<int64_t>(c, 2048);
+  c = std::max<int64_t>(c, 4096);
   c = std::min<int64_t>(c, 8192);
+  const int64_t Vp = cdiv(V, kTile) * kTile;
+  while (c > 256 && c * Vp * es > (int64_t)1500000000) c /= 2;
   return std::min(c, N);
 }
 
@@ -161,7 +168,7 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.N = N;
   p.H = H;
   p.V = V;
-  p.C = effective_chunk(N, H, V, chunk);
+  p.C = effective_chunk(N, H, V, chunk, (int64_t)in_size(cfg));
   p.Vp = cdiv(V, kTile) * kTile;
   p.tiles_v = (int)(p.Vp / kTile);
   p.tiles_h = (int)cdiv(H, kTile);
@@ -223,7 +230,7 @@ flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int
   if (st != FLCE_OK) return st;
   const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
   const int64_t es = (int64_t)in_size(cfg);
-  const int64_t C = effective_chunk(N, H, V, chunk);
+  const int64_t C = effective_chunk(N, H, V, chunk, es);
   const int64_t Vp = cdiv(V, kTile) * kTile;
   if (V * H * es >= lim || C * H * es >= lim || C * Vp * es >= lim) return FLCE_ERR_UNSUPPORTED;
   return FLCE_OK;
@@ -411,7 +418,7 @@ flce_status_t flce_destroy(flce_handle_t h) {
 }
 
 int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk) {
-  return effective_chunk(N, H, V, chunk);
+  return effective_chunk(N, H, V, chunk, 2);
 }
 
 size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {

@@ -46,10 +46,12 @@ def test_effective_chunk_rule():
     # explicit chunks are clamped to [1, N]
     assert flce.flce_effective_chunk(1000, 512, 5000, 384) == 384
     assert flce.flce_effective_chunk(100, 512, 5000, 384) == 100
-    # automatic: next_pow2(ceil(N / ceil(V/H))) raised to 2048, capped at 8192 and at N
-    assert flce.flce_effective_chunk(16384, 4096, 128256, 0) == 2048     # page rule gives 512
+    # automatic: next_pow2(ceil(N / ceil(V/H))) raised to 4096, capped at 8192, at a 1.5 GB
+    # logits buffer and at N
+    assert flce.flce_effective_chunk(16384, 4096, 128256, 0) == 4096     # page rule gives 512
     assert flce.flce_effective_chunk(131072, 4096, 128256, 0) == 4096
     assert flce.flce_effective_chunk(1 << 20, 4096, 32000, 0) == 8192
+    assert flce.flce_effective_chunk(1 << 20, 4096, 256000, 0) == 2048  # 4096 x 256000 x 2 B > 1.5 GB
     assert flce.flce_effective_chunk(256, 256, 4096, 0) == 256
     assert flce.flce_effective_chunk(0, 256, 4096, 0) == 0
 
