@@ -116,6 +116,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_vocab")
     ap.add_argument("--chunk", type=int, default=0, help="0 = the workload's chunk")
+    ap.add_argument("--variant", choices=["chunked", "fused"], default="chunked")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="also measure the peak HBM of the materialised-logits PyTorch path")
@@ -155,7 +156,8 @@ def main():
 
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
-    f = flce.FusedLinearCrossEntropy(in_dtype=tdt)
+    variant = flce.FLCE_FUSED if args.variant == "fused" else flce.FLCE_CHUNKED
+    f = flce.FusedLinearCrossEntropy(in_dtype=tdt, variant=variant)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     dx = torch.empty_like(x)
     dW = torch.empty_like(W)
@@ -244,7 +246,7 @@ def main():
         "data": "synthetic (seeded x~N(0,1), W~N(0,0.02^2), targets "
                 + ("Zipf(1.1)" if w.targets == "zipf" else "uniform") + ")",
         "config": {"workload": f"{w.name}: N={w.N} H={w.H} V={w.V} {w.dtype}, chunk {eff_chunk}",
-                   "N": w.N, "H": w.H, "V": w.V, "chunk": eff_chunk, "variant": "chunked",
+                   "N": w.N, "H": w.H, "V": w.V, "chunk": eff_chunk, "variant": args.variant,
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,

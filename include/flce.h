@@ -52,7 +52,11 @@ typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype_t;
 
 typedef enum {
   FLCE_CHUNKED = 0,           /* token chunks; one [C,V] buffer overwritten in place by dlogits */
-  FLCE_FUSED = 1              /* reserved for the two-pass fused variant (not built: FLCE_ERR_UNSUPPORTED) */
+  FLCE_FUSED = 1              /* two passes, no logits buffer: pass 1 per-token log-sum-exp; pass 2
+                                 recomputes each logits tile, keeps its dlogits on chip and adds the
+                                 dx / dW partials into fp32 accumulators with atomics.  bf16 inputs
+                                 only.  With bf16 dW the accumulator is an extra V*H*4 bytes; with
+                                 fp32 dW it is dW itself.  Results are not bitwise repeatable. */
 } flce_variant_t;
 
 typedef struct {
@@ -68,8 +72,8 @@ typedef struct {
 typedef struct flce_handle_s* flce_handle_t;
 
 /* Creates a handle.  No device memory is allocated yet.
- * Errors: INVALID_ARG (null cfg/out, bad enum), UNSUPPORTED (fp32 inputs with a bf16 output),
- *         HIP (device ordinal not usable). */
+ * Errors: INVALID_ARG (null cfg/out, bad enum), UNSUPPORTED (fp32 inputs with a bf16 output, or
+ *         the fused variant with fp32 inputs), HIP (device ordinal not usable). */
 flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
 
 /* Frees the handle's workspace (device-synchronising) and the handle.  NULL is a no-op. */

@@ -36,6 +36,8 @@ struct Plan {
   int splits = 1;
   int64_t k_per_split = 0;
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
+  size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
+  bool fused = false;
   size_t total = 0;
 };
 
@@ -43,9 +45,11 @@ struct Plan {
 
 namespace {
 
-enum Kernel { K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"logits_lse", "lse_combine", "dlogits", "dx",
-                                           "dx_reduce", "dw", "finalize"};
+enum Kernel {
+  K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_FUSED_BWD, K_FILL, K_CAST, K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {"logits_lse", "lse_combine", "dlogits", "dx", "dx_reduce",
+                                           "dw", "finalize", "fused_bwd", "fill_zero", "cast_bf16"};
 
 struct Mark {
   int kind;                 // Kernel, or -1 for the event that closes a call
@@ -182,15 +186,21 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.splits = (int)s;
   p.k_per_split = cdiv(cdiv(p.Vp, s), bk) * bk;
 
+  p.fused = cfg.variant == FLCE_FUSED;
   size_t off = 0;
-  p.off_z = off;    off = align_up(off + (size_t)p.C * p.Vp * in_size(cfg));
+  p.off_z = off;
+  if (!p.fused) off = align_up(off + (size_t)p.C * p.Vp * in_size(cfg));
   p.off_pm = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
   p.off_ps = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
   p.off_zt = off;   off = align_up(off + (size_t)N * sizeof(float));
   p.off_lse = off;  off = align_up(off + (size_t)N * sizeof(float));
   p.off_loss = off; off = align_up(off + (size_t)N * sizeof(float));
   p.off_part = off;
-  if (p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
+  if (!p.fused && p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
+  p.off_dxacc = off;
+  if (p.fused && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
+  p.off_dwacc = off;
+  if (p.fused && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
   p.total = off;
   return p;
 }
@@ -367,6 +377,107 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
   return FLCE_OK;
 }
 
+// Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and pass 2
+// (recompute, dlogits in LDS, dx and dW partials by fp32 atomics); outputs converted last.
+flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const void* W, const int64_t* t,
+                        float* loss, void* dx, void* dW, float* lse_out, hipStream_t st) {
+  const flce_config_t& cfg = h->cfg;
+  char* ws = static_cast<char*>(h->ws);
+  float* pm = reinterpret_cast<float*>(ws + p.off_pm);
+  float* ps = reinterpret_cast<float*>(ws + p.off_ps);
+  float* zt = reinterpret_cast<float*>(ws + p.off_zt);
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
+  float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
+  const bool dx32 = cfg.dx_dtype == FLCE_FP32, dw32 = cfg.dw_dtype == FLCE_FP32;
+  float* dw_acc = dw32 ? static_cast<float*>(dW) : reinterpret_cast<float*>(ws + p.off_dwacc);
+  const float inv_n = (float)(1.0 / (double)p.N);
+  const double VH = (double)p.V * (double)p.H;
+
+  flce::FillArgs zw{dw_acc, p.V * p.H};
+  FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * VH, st));
+  FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
+  for (int64_t s = 0; s < p.N; s += p.C) {
+    const int rows = (int)std::min(p.C, p.N - s);
+    const int tiles_m = (int)cdiv(rows, kTile);
+    const double gemm_flops = 2.0 * rows * VH;
+    const void* xs = static_cast<const char*>(x) + (size_t)s * p.H * 2;
+
+    flce::LogitsArgs la{};
+    la.x = xs;
+    la.W = W;
+    la.t = t + s;
+    la.z = nullptr;
+    la.pm = pm;
+    la.ps = ps;
+    la.zt = zt + s;
+    la.ldz = p.Vp;
+    la.pstride = (int)p.C;
+    la.rows = rows;
+    la.H = (int)p.H;
+    la.V = (int)p.V;
+    la.tiles_m = tiles_m;
+    la.tiles_n = p.tiles_v;
+    FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * 2 + VH * 2, st));
+    FLCE_LAUNCH(flce::launch_logits(In::BF16, la, st));
+
+    flce::CombineArgs ca{};
+    ca.pm = pm;
+    ca.ps = ps;
+    ca.zt = zt + s;
+    ca.t = t + s;
+    ca.lse = lse + s;
+    ca.loss_rows = loss_rows + s;
+    ca.flag = h->flag;
+    ca.pstride = (int)p.C;
+    ca.tiles_n = p.tiles_v;
+    ca.rows = rows;
+    ca.V = (int)p.V;
+    FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
+    FLCE_LAUNCH(flce::launch_combine(ca, st));
+
+    float* dx_acc = dx32 ? static_cast<float*>(dx) + (size_t)s * p.H : reinterpret_cast<float*>(ws + p.off_dxacc);
+    flce::FillArgs zx{dx_acc, (int64_t)rows * p.H};
+    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * rows * p.H, st));
+    FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
+
+    flce::FusedArgs fa{};
+    fa.x = xs;
+    fa.W = W;
+    fa.t = t + s;
+    fa.lse = lse + s;
+    fa.dx_acc = dx_acc;
+    fa.dw_acc = dw_acc;
+    fa.rows = rows;
+    fa.H = (int)p.H;
+    fa.V = (int)p.V;
+    fa.tiles_m = tiles_m;
+    fa.tiles_n = p.tiles_v;
+    fa.tiles_h = p.tiles_h;
+    fa.inv_n = inv_n;
+    // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
+    FLCE_LAUNCH(mark(h, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
+    FLCE_LAUNCH(flce::launch_fused_bwd(fa, st));
+    if (!dx32) {
+      flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H};
+      FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * rows * p.H, st));
+      FLCE_LAUNCH(flce::launch_cast_bf16(cx, st));
+    }
+  }
+  if (!dw32) {
+    flce::CastArgs cw{dw_acc, dW, p.V * p.H};
+    FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * VH, st));
+    FLCE_LAUNCH(flce::launch_cast_bf16(cw, st));
+  }
+  flce::FinalizeArgs fa{};
+  fa.loss_rows = loss_rows;
+  fa.loss = loss;
+  fa.n = p.N;
+  FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
+  FLCE_LAUNCH(flce::launch_finalize(fa, st));
+  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,7 +502,7 @@ flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out) {
   if (cfg->reserved != 0 || cfg->workspace_limit < 0 || cfg->device < 0) return FLCE_ERR_INVALID_ARG;
   if (cfg->in_dtype == FLCE_FP32 && (cfg->dx_dtype != FLCE_FP32 || cfg->dw_dtype != FLCE_FP32))
     return FLCE_ERR_UNSUPPORTED;
-  if (cfg->variant == FLCE_FUSED) return FLCE_ERR_UNSUPPORTED;
+  if (cfg->variant == FLCE_FUSED && cfg->in_dtype != FLCE_BF16) return FLCE_ERR_UNSUPPORTED;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || cfg->device >= ndev) {
     (void)hipGetLastError();
@@ -452,6 +563,7 @@ flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const voi
   if (ws != FLCE_OK) return ws;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  if (p.fused) return run_fused(h, p, x, W, targets, loss, dx, dW, lse, static_cast<hipStream_t>(stream));
   return run_chunked(h, p, x, W, targets, loss, dx, dW, lse, static_cast<hipStream_t>(stream));
 }
 

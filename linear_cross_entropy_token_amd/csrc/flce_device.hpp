@@ -113,16 +113,18 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, char* lds, uint32_t voff) {
 __device__ __forceinline__ int swz_k(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 __device__ __forceinline__ int swz_mn(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
 
-// One operand: 256 indices along its "mn" dimension by one k-slice per stage.
-// KMAJOR: stored [mn][k] (k contiguous).  Otherwise stored [k][mn] (mn contiguous).
-template <typename T, bool KMAJOR>
+// One operand: 256 indices along its "mn" dimension by one k-slice per stage, copied as
+// 4 x BPW blocks of 1 KiB (BPW per wave).  KMAJOR: stored [mn][k] (k contiguous); otherwise
+// stored [k][mn] (mn contiguous).  With BPW < kBlocksPerWave an mn-major slice holds fewer
+// k-rows (2 per block for bf16).
+template <typename T, bool KMAJOR, int BPW = kBlocksPerWave>
 struct Operand {
   static constexpr bool kKMajor = KMAJOR;
   static constexpr int E = Elem<T>::E;
   static constexpr int ES = (int)sizeof(T);
   i32x4 rsrc;
-  uint32_t base[kBlocksPerWave];  // byte offset of this lane's 16 bytes at k = 0 (kOOB if mn is out of range)
-  int kpos[kBlocksPerWave];       // k offset (within a slice) of this lane's data, for the k bound
+  uint32_t base[BPW];  // byte offset of this lane's 16 bytes at k = 0 (kOOB if mn is out of range)
+  int kpos[BPW];       // k offset (within a slice) of this lane's data, for the k bound
   uint32_t kstride;     // bytes per unit of k
 
   // ld: row stride (elements); mn_end: valid mn extent; rows beyond the buffer read as zero.
@@ -131,8 +133,8 @@ struct Operand {
     rsrc = make_rsrc(ptr, bytes);
     kstride = KMAJOR ? (uint32_t)ES : (uint32_t)(ld * ES);
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) {
-      const int b = wave * kBlocksPerWave + i;       // 1 KiB block of the operand's stage
+    for (int i = 0; i < BPW; ++i) {
+      const int b = wave * BPW + i;                  // 1 KiB block of the operand's stage
       if constexpr (KMAJOR) {
         const int row = 8 * b + (lane >> 3);
         const int c = (lane & 7) ^ swz_k(row);
@@ -158,10 +160,10 @@ struct Operand {
   // Copies the slice starting at contraction index k0 (k < k_end valid) into lds_op.
   __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave) const {
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) {
+    for (int i = 0; i < BPW; ++i) {
       const bool ok = base[i] != kOOB && k0 + kpos[i] < k_end;
       const uint32_t v = ok ? base[i] + (uint32_t)k0 * kstride : kOOB;
-      dma16(rsrc, lds_op + (wave * kBlocksPerWave + i) * 1024, v);
+      dma16(rsrc, lds_op + (wave * BPW + i) * 1024, v);
     }
   }
 };
@@ -277,6 +279,19 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const
     }
   }
   __syncthreads();   // LDS free for the epilogue
+}
+
+// Output coordinates of accumulator (i, j, q) in this lane: the 4 consecutive
+// columns col0 .. col0 + 3 of one row (see the engine header).
+struct Frag {
+  int rowb, colb, lane;
+  __device__ __forceinline__ int row(int j) const { return rowb + 32 * j + (lane & 31); }
+  __device__ __forceinline__ int col0(int i, int q) const { return colb + 32 * i + 8 * q + 4 * (lane >> 5); }
+};
+__device__ __forceinline__ Frag frag_coords() {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  return Frag{(wave >> 1) * 128, (wave & 1) * 128, tid & 63};
 }
 
 // Maps the hardware workgroup index to a logical tile index so that each of

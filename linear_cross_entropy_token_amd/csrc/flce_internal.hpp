@@ -85,6 +85,31 @@ struct FinalizeArgs {
   int64_t n;
 };
 
+// Fused variant, pass 2: per (token tile, vocabulary tile) the logits tile is recomputed,
+// turned into dlogits in LDS, and fed straight into dx and dW updates (fp32 atomics).
+struct FusedArgs {
+  const void* x;        // chunk's first token row [rows][H] (bf16)
+  const void* W;        // [V][H] (bf16)
+  const int64_t* t;     // chunk's targets [rows]
+  const float* lse;     // chunk's per-row log-sum-exp [rows]
+  float* dx_acc;        // fp32 [rows][H], zeroed before the launch
+  float* dw_acc;        // fp32 [V][H], zeroed before the first chunk
+  int rows, H, V;
+  int tiles_m, tiles_n, tiles_h;
+  float inv_n;
+};
+
+struct FillArgs {
+  float* p;
+  int64_t n;            // multiple of 4
+};
+
+struct CastArgs {       // fp32 -> bf16, round to nearest even
+  const float* src;
+  void* dst;
+  int64_t n;            // multiple of 4
+};
+
 hipError_t launch_logits(In in, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_dlogits(In in, const DlogitsArgs& a, hipStream_t s);
@@ -92,5 +117,8 @@ hipError_t launch_dx(In in, const DxArgs& a, hipStream_t s);
 hipError_t launch_dx_reduce(const DxReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(In in, const DwArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
+hipError_t launch_fused_bwd(const FusedArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(const FillArgs& a, hipStream_t s);
+hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t s);
 
 }  // namespace flce

@@ -21,19 +21,6 @@ namespace flce {
 
 static_assert(kTile == kTileM && kTile == kTileN, "tile sizes of the dispatcher and the engine differ");
 
-// Output coordinates of accumulator (i, j, q) in this lane: the 4 consecutive
-// columns col0 .. col0 + 3 of one row (see the engine header).
-struct Frag {
-  int rowb, colb, lane;
-  __device__ __forceinline__ int row(int j) const { return rowb + 32 * j + (lane & 31); }
-  __device__ __forceinline__ int col0(int i, int q) const { return colb + 32 * i + 8 * q + 4 * (lane >> 5); }
-};
-__device__ __forceinline__ Frag frag_coords() {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  return Frag{(wave >> 1) * 128, (wave & 1) * 128, tid & 63};
-}
-
 // ---------------------------------------------------------------------------
 // logits + LSE partials + target gather + z store
 // ---------------------------------------------------------------------------
@@ -106,6 +93,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (c0 + e == tr) a.zt[grow] = acc[i][j][4 * q + e];
+          if (Z == nullptr) continue;   // statistics-only pass
           if constexpr (ES == 2) {
             u32x2 v{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};

@@ -31,11 +31,13 @@ def to_f64(ten):
     return ten.detach().to("cpu", torch.float32).numpy().astype(np.float64)
 
 
-def run_flce(d, chunk=0, dx_dtype=None, dw_dtype=None, with_lse=False, dev="cuda:0", handle=None):
+def run_flce(d, chunk=0, dx_dtype=None, dw_dtype=None, with_lse=False, dev="cuda:0", handle=None,
+             variant=0):
     import torch
     from linear_cross_entropy_token_amd import FusedLinearCrossEntropy
     x, W, t = to_device(d, dev)
-    f = handle or FusedLinearCrossEntropy(in_dtype=x.dtype, dx_dtype=dx_dtype, dw_dtype=dw_dtype)
+    f = handle or FusedLinearCrossEntropy(in_dtype=x.dtype, dx_dtype=dx_dtype, dw_dtype=dw_dtype,
+                                          variant=variant)
     out = f.forward_backward(x, W, t, chunk=chunk, with_lse=with_lse)
     torch.cuda.synchronize()
     res = {"loss": float(out[0].item()), "dx": to_f64(out[1]), "dW": to_f64(out[2])}
