@@ -73,7 +73,7 @@ def cpu_baseline(w, seconds_target: float = 15.0):
     t0 = time.perf_counter()
     oracle.flce(x, W, d["t"])
     dt = time.perf_counter() - t0
-    n2 = int(min(2048, max(n, n * seconds_target / max(dt, 1e-3))))
+    n2 = int(min(8192, max(n, n * seconds_target / max(dt, 1e-3))))
     n2 = max(n, (n2 // 64) * 64)
     if n2 > n:
         d = make_inputs(n2, w.H, w.V, w.dtype, w.seed, w.targets)

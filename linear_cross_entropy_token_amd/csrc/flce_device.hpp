@@ -2,8 +2,8 @@
 //
 // Every dense contraction of the path (logits = x W^T, dx = G W, dW = G^T x)
 // runs on one MFMA tile engine:
-//  * a 256-thread workgroup (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
-//    each wave owns 128 x 128 as 4 x 4 blocks of 32 x 32 accumulated in fp32
+//  * a 512-thread workgroup (8 wave64s, 2 x 4) owns a 256 x 256 output tile;
+//    each wave owns 128 x 64 as 2 x 4 blocks of 32 x 32 accumulated in fp32
 //    by v_mfma_f32_32x32x16_bf16 (bf16 inputs) or v_mfma_f32_32x32x2_f32
 //    (fp32 inputs);
 //  * the contraction is walked in k-slices of 128 bytes per operand row
@@ -45,14 +45,21 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 typedef uint16_t bf16_t;   // bf16 storage (raw bits)
 
-constexpr int kThreads = 256;
+// Eight waves (two per SIMD) per 256 x 256 tile, each owning 128 rows x 64 columns
+// (128 accumulator registers): while one wave of a SIMD waits on its copies or the
+// barrier, the other keeps the matrix core busy (measured 4-11% faster than four waves
+// of 128 x 128 on all three GEMMs).
+constexpr int kWaves = 8;                           // waves per workgroup (2 rows x kWaveCols)
+constexpr int kWaveCols = kWaves / 2;
+constexpr int kColBlocks = 256 / kWaveCols / 32;    // 32-column MFMA blocks per wave
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 256;             // output tile is kTile x kTile
 constexpr int kStages = 2;                          // LDS ring depth
 constexpr int kSliceBytes = kSliceBytesABI;         // bytes of one k-major operand row per slice
 constexpr int kOpBytes = kTile * kSliceBytes;       // one operand's part of a stage (32 KiB)
 constexpr int kStageBytes = 2 * kOpBytes;
 constexpr int kSmemBytes = kStages * kStageBytes;   // 128 KiB
-constexpr int kBlocksPerWave = kOpBytes / 1024 / 4; // 1 KiB DMA blocks per wave per operand and slice
+constexpr int kBlocksPerWave = kOpBytes / 1024 / kWaves; // 1 KiB DMA blocks per wave per operand and slice
 constexpr int kSteps = kSliceBytes / 32;            // MFMA k-steps per slice
 constexpr uint32_t kOOB = 0xFFFFFF00u; // buffer offset beyond every valid range -> zeros
 constexpr float kLog2e = 1.4426950408889634f;
@@ -219,6 +226,7 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 template <int N>
 __device__ __forceinline__ void sync_slice() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "unsupported vmcnt");
@@ -227,16 +235,16 @@ __device__ __forceinline__ void sync_slice() {
 // acc[i][j] += sum over k in [k_begin, k_end) of C[col 32i + ..][k] * R[row 32j + ..][k] for the
 // wave's 128 x 128 part of the tile.  Col and Row fill their halves of each LDS stage.
 template <typename T, class OpC, class OpR>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const OpC& C, const OpR& R,
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C, const OpR& R,
                                           int k_begin, int k_end) {
   constexpr int BK = slice_k<T>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rowb = (wave >> 1) * 128;
-  const int colb = (wave & 1) * 128;
+  const int rowb = (wave / kWaveCols) * 128;
+  const int colb = (wave % kWaveCols) * (kTile / kWaveCols);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -267,13 +275,13 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], char* smem, const
     const char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      u32x4 a[4], b[4];
+      u32x4 a[kColBlocks], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
+      for (int i = 0; i < kColBlocks; ++i) a[i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = read_frag<T, OpR::kKMajor>(st + kOpBytes, rowb + 32 * j, s, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(a[i], b[j], acc[i][j]);
     }
@@ -291,8 +299,23 @@ struct Frag {
 __device__ __forceinline__ Frag frag_coords() {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  return Frag{(wave >> 1) * 128, (wave & 1) * 128, tid & 63};
+  return Frag{(wave / kWaveCols) * 128, (wave % kWaveCols) * (kTile / kWaveCols), tid & 63};
 }
+
+// Logical tile L -> (tm, tn): tiles walk m fastest inside groups of gm m-tiles that sweep
+// all n, so the 32 tiles one XCD runs at a time form a gm x (32 / gm) block whose operand
+// slices are shared in that XCD's L2 (4 x 8 needs 12 tile-slices of operands per k-step
+// instead of 2 x 16's 18).
+__device__ __forceinline__ void grouped_tile(int L, int TM, int TN, int gm, int& tm, int& tn) {
+  const int per_group = gm * TN;
+  const int g = L / per_group;
+  const int first = g * gm;
+  const int rows = min(TM - first, gm);
+  const int r = L - g * per_group;
+  tm = first + r % rows;
+  tn = r / rows;
+}
+constexpr int kGroupM = 4;
 
 // Maps the hardware workgroup index to a logical tile index so that each of
 // the 8 XCDs (workgroups are dealt to XCDs round-robin) works on one

@@ -58,16 +58,19 @@ constexpr int kStreamBytes = 16384;   // one 32-row mn-major slice of a 256-wide
 //   row = 32 j + 8 (rg / 4) + 4 (l / 32) + rg % 4,   col = 32 i + l % 32,
 // i.e. the 32 lanes of a half-wave hold 32 consecutive columns of one row, and each atomic
 // instruction of the epilogue touches two 128-byte lines.
+constexpr int kStreamBPW = 16 / kWaves;   // 1 KiB DMA blocks per wave per streamed slice
+
 template <class RowsFrag>
-__device__ __forceinline__ void gemm_stream(f32x16 (&acc)[4][4], char* ring, const Operand<bf16_t, false, 4>& S,
-                                            int k_end, RowsFrag rows_frag) {
+__device__ __forceinline__ void gemm_stream(f32x16 (&acc)[kColBlocks][4], char* ring,
+                                            const Operand<bf16_t, false, kStreamBPW>& S, int k_end,
+                                            RowsFrag rows_frag) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rowb = (wave >> 1) * 128;
-  const int colb = (wave & 1) * 128;
+  const int rowb = (wave / kWaveCols) * 128;
+  const int colb = (wave % kWaveCols) * (kTile / kWaveCols);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -79,13 +82,13 @@ __device__ __forceinline__ void gemm_stream(f32x16 (&acc)[4][4], char* ring, con
     const char* st = ring + (kt & 1) * kStreamBytes;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      u32x4 a[4], b[4];
+      u32x4 a[kColBlocks], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = read_frag<bf16_t, false>(st, colb + 32 * i, s, lane);
+      for (int i = 0; i < kColBlocks; ++i) a[i] = read_frag<bf16_t, false>(st, colb + 32 * i, s, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = rows_frag(rowb + 32 * j, 2 * kt + s, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma<bf16_t>(b[j], a[i], acc[i][j]);
     }
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
 
   // 1. z tile (columns: vocabulary, rows: tokens)
-  f32x16 acc[4][4];
+  f32x16 acc[kColBlocks][4];
   {
     Operand<bf16_t, true> C, R;
     C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2), wave, lane);
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
     const float l = rok ? a.lse[tok] : 0.f;
     const int64_t tv = rok ? a.t[tok] : -1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c0 = f.col0(i, q);
@@ -153,11 +156,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
   for (int hb = 0; hb < a.tiles_h; ++hb) {
     const int h0 = hb * kTile;
     {
-      Operand<bf16_t, false, 4> S;           // W[n0 + v][h0 + h], contraction over v
+      Operand<bf16_t, false, kStreamBPW> S;           // W[n0 + v][h0 + h], contraction over v
       S.init(W + (int64_t)n0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kv * a.H * 2), wave, lane);
       gemm_stream(acc, ring, S, kv, [&](int mnb, int ks, int ln) { return g_frag_k(g, mnb, ks, ln); });
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kColBlocks; ++i) {
         const int h = h0 + f.colb + 32 * i + (lane & 31);
         if (h >= a.H) continue;
 #pragma unroll
@@ -170,11 +173,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
       }
     }
     {
-      Operand<bf16_t, false, 4> S;           // x[m0 + token][h0 + h], contraction over tokens
+      Operand<bf16_t, false, kStreamBPW> S;           // x[m0 + token][h0 + h], contraction over tokens
       S.init(X + (int64_t)m0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kt_ * a.H * 2), wave, lane);
       gemm_stream(acc, ring, S, kt_, [&](int mnb, int ks, int ln) { return g_frag_t(g, mnb, ks, ln); });
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kColBlocks; ++i) {
         const int h = h0 + f.colb + 32 * i + (lane & 31);
         if (h >= a.H) continue;
 #pragma unroll

@@ -29,8 +29,8 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int tid = threadIdx.x;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
-  const int tm = L % a.tiles_m;
-  const int tn = L / a.tiles_m;
+  int tm, tn;
+  grouped_tile(L, a.tiles_m, a.tiles_n, kGroupM, tm, tn);
   const int m0 = tm * kTile;   // tokens
   const int n0 = tn * kTile;   // vocabulary ids
   constexpr int ES = (int)sizeof(T);
@@ -39,13 +39,13 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   C.init(static_cast<const T*>(a.W), a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
   R.init(static_cast<const T*>(a.x), a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6,
          tid & 63);
-  f32x16 acc[4][4];
+  f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, 0, a.H);
 
   const Frag f = frag_coords();
-  float* red = reinterpret_cast<float*>(smem);                 // [4][kTile]: max wc0, max wc1, sum wc0, sum wc1
-  int* trel = reinterpret_cast<int*>(smem + 4 * kTile * sizeof(float));
-  {
+  float* red = reinterpret_cast<float*>(smem);   // [2][kWaveCols][kTile]: per column-wave max, then sum
+  int* trel = reinterpret_cast<int*>(smem + 2 * kWaveCols * kTile * sizeof(float));
+  if (tid < kTile) {
     const int r = m0 + tid;
     int rel = -1;
     if (r < a.rows) {
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   __syncthreads();
 
   const float ninf = -__builtin_inff();
-  const int wc = (tid >> 6) & 1;
+  const int wc = (tid >> 6) % kWaveCols;
   const int vlim = a.V - n0;                // columns >= vlim are padding
   T* Z = static_cast<T*>(a.z);
 #pragma unroll
@@ -66,27 +66,27 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
     const int grow = m0 + row;
     float mx = ninf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int rg = 0; rg < 16; ++rg)
         if (f.col0(i, rg >> 2) + (rg & 3) < vlim) mx = fmaxf(mx, acc[i][j][rg]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int rg = 0; rg < 16; ++rg)
         if (f.col0(i, rg >> 2) + (rg & 3) < vlim) s += fast_exp(acc[i][j][rg] - mx);
     s += __shfl_xor(s, 32, 64);
     if (f.lane < 32) {
       red[wc * kTile + row] = mx;
-      red[(2 + wc) * kTile + row] = s;
+      red[(kWaveCols + wc) * kTile + row] = s;
     }
     if (grow < a.rows) {
       const int tr = trel[row];
       T* zrow = Z + (int64_t)grow * a.ldz + n0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kColBlocks; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c0 = f.col0(i, q);
@@ -107,11 +107,16 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
     }
   }
   __syncthreads();
-  if (m0 + tid < a.rows) {
-    const float M0 = red[tid], M1 = red[kTile + tid];
-    const float S0 = red[2 * kTile + tid], S1 = red[3 * kTile + tid];
-    const float M = fmaxf(M0, M1);
-    const float S = (M0 == ninf ? 0.f : S0 * fast_exp(M0 - M)) + (M1 == ninf ? 0.f : S1 * fast_exp(M1 - M));
+  if (tid < kTile && m0 + tid < a.rows) {
+    float M = ninf;
+#pragma unroll
+    for (int w = 0; w < kWaveCols; ++w) M = fmaxf(M, red[w * kTile + tid]);
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaveCols; ++w) {
+      const float m = red[w * kTile + tid];
+      if (m != ninf) S += red[(kWaveCols + w) * kTile + tid] * fast_exp(m - M);
+    }
     a.pm[(int64_t)tn * a.pstride + m0 + tid] = M;
     a.ps[(int64_t)tn * a.pstride + m0 + tid] = S;
   }
@@ -202,8 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   const int L = xcd_remap(blockIdx.x, tiles * a.splits);
   const int split = L / tiles;
   const int rem = L - split * tiles;
-  const int tn = rem % a.tiles_n;
-  const int tm = rem / a.tiles_n;
+  int tm, tn;
+  grouped_tile(rem, a.tiles_m, a.tiles_n, kGroupM, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;   // tokens, hidden units
   const int ks = split * a.k_per_split;
   const int ke = (int)min((int64_t)ks + a.k_per_split, a.ldg);
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
   R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES), tid >> 6,
          tid & 63);
-  f32x16 acc[4][4];
+  f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, ks, ke);
 
   const Frag f = frag_coords();
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
     const int grow = m0 + f.row(j);
     if (grow >= a.rows) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = n0 + f.col0(i, q);
@@ -264,8 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int tid = threadIdx.x;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
-  const int tn = L % a.tiles_n;
-  const int tm = L / a.tiles_n;
+  int tm, tn;
+  grouped_tile(L, a.tiles_m, a.tiles_n, kGroupM, tm, tn);
   const int m0 = tm * kTile, n0 = tn * kTile;   // vocabulary ids, hidden units
   constexpr int ES = (int)sizeof(T);
 
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   C.init(static_cast<const T*>(a.x), a.H, n0, a.H, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6, tid & 63);
   R.init(static_cast<const T*>(a.g), a.ldg, m0, (int)a.ldg, (uint32_t)((int64_t)a.rows * a.ldg * ES),
          tid >> 6, tid & 63);
-  f32x16 acc[4][4];
+  f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, 0, a.rows);
 
   const Frag f = frag_coords();
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
     const int v = m0 + f.row(j);
     if (v >= a.V) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int h = n0 + f.col0(i, q);
