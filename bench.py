@@ -117,6 +117,8 @@ def main():
     ap.add_argument("--workload", default="llama3_vocab")
     ap.add_argument("--chunk", type=int, default=0, help="0 = the workload's chunk")
     ap.add_argument("--variant", choices=["chunked", "fused"], default="chunked")
+    ap.add_argument("--grad-dtype", choices=["input", "fp32"], default="input",
+                    help="dtype of dx and dW (default: the input dtype)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="also measure the peak HBM of the materialised-logits PyTorch path")
@@ -157,10 +159,11 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     variant = flce.FLCE_FUSED if args.variant == "fused" else flce.FLCE_CHUNKED
-    f = flce.FusedLinearCrossEntropy(in_dtype=tdt, variant=variant)
+    gdt = torch.float32 if args.grad_dtype == "fp32" else tdt
+    f = flce.FusedLinearCrossEntropy(in_dtype=tdt, dx_dtype=gdt, dw_dtype=gdt, variant=variant)
     loss = torch.empty((), dtype=torch.float32, device=dev)
-    dx = torch.empty_like(x)
-    dW = torch.empty_like(W)
+    dx = torch.empty(x.shape, dtype=gdt, device=dev)
+    dW = torch.empty(W.shape, dtype=gdt, device=dev)
     base_alloc = torch.cuda.memory_allocated()
     free0, _ = torch.cuda.mem_get_info()
     f.reserve(w.N, w.H, w.V, chunk)
@@ -247,6 +250,7 @@ def main():
                 + ("Zipf(1.1)" if w.targets == "zipf" else "uniform") + ")",
         "config": {"workload": f"{w.name}: N={w.N} H={w.H} V={w.V} {w.dtype}, chunk {eff_chunk}",
                    "N": w.N, "H": w.H, "V": w.V, "chunk": eff_chunk, "variant": args.variant,
+                   "grad_dtype": "fp32" if args.grad_dtype == "fp32" else w.dtype,
                    "parallelism": "single GPU"},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
