@@ -46,9 +46,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;   // bf16 storage (raw bits)
 
 // Eight waves (two per SIMD) per 256 x 256 tile, each owning 128 rows x 64 columns
-// (128 accumulator registers): while one wave of a SIMD waits on its copies or the
-// barrier, the other keeps the matrix core busy (measured 4-11% faster than four waves
-// of 128 x 128 on all three GEMMs).
+// (128 accumulator registers + 96 fragment registers for one k-slice); the two waves of a
+// SIMD alternate between multiplying and reading LDS (the ping-pong schedule of gemm_tile).
 constexpr int kWaves = 8;                           // waves per workgroup (2 rows x kWaveCols)
 constexpr int kWaveCols = kWaves / 2;
 constexpr int kColBlocks = 256 / kWaveCols / 32;    // 32-column MFMA blocks per wave
@@ -219,24 +218,35 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-// Waits until at most N of this wave's direct-to-LDS copies are in flight, then
-// joins the workgroup barrier.  One asm statement, so the compiler moves no
-// memory access across it; the plain barrier carries no fence, which would
-// force vmcnt(0) and drain the copies of the later slices.
-template <int N>
-__device__ __forceinline__ void sync_slice() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 0, "unsupported vmcnt");
+// Joins the workgroup barrier after this wave's outstanding copies (vmcnt) and/or LDS reads
+// (lgkmcnt) have completed.  One asm statement between two scheduling barriers, so the compiler
+// moves no instruction (memory access or MFMA) across it; the plain barrier carries no fence.
+template <bool VM, bool LGKM>
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (VM && LGKM) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (VM) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (LGKM) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // acc[i][j] += sum over k in [k_begin, k_end) of C[col 32i + ..][k] * R[row 32j + ..][k] for the
-// wave's 128 x 128 part of the tile.  Col and Row fill their halves of each LDS stage.
+// wave's 128 x 64 part of the tile.  C and R fill their halves of each LDS stage.
+//
+// Ping-pong schedule.  The two waves of a SIMD (wave w and w + 4) take turns: in each phase
+// (one barrier interval) one of them runs the 4 x kColBlocks x 4 MFMAs of a whole k-slice from
+// registers while the other reads its fragments of the next slice from LDS and issues
+// copies, so the matrix core never waits for the LDS pipe of its own wave.  With phases
+// numbered from 0, waves 0-3 read slice kt in phase 2kt and multiply in 2kt+1; waves 4-7
+// read it in 2kt+1 and multiply in 2kt+2.  Slice kt+1 is copied into the other stage
+// during phases 2kt and 2kt+1 (each wave copies its share at the start of phase 2kt; both
+// readers of the slice it replaces finished by phase 2kt-1) and every wave waits for its
+// copies at the end of phase 2kt+1.  There are 2 nk + 1 phases per tile.
 template <typename T, class OpC, class OpR>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C, const OpR& R,
                                           int k_begin, int k_end) {
+  static_assert(kStages == 2 && kWaves == 8, "the ping-pong schedule pairs the waves of a SIMD over two stages");
   constexpr int BK = slice_k<T>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -250,25 +260,86 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % kStages) * kStageBytes;
+    const int k0 = k_begin + kt * BK;
+    C.issue(st, k0, k_end, wave);
+    R.issue(st + kOpBytes, k0, k_end, wave);
+  };
+  u32x4 fa[kSteps][kColBlocks], fb[kSteps][4];
+  auto read = [&](int kt) {
+    const char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (s < nk) {
-      char* st = smem + s * kStageBytes;
-      C.issue(st, k_begin + s * BK, k_end, wave);
-      R.issue(st + kOpBytes, k_begin + s * BK, k_end, wave);
+    for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i) fa[s][i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[s][j] = read_frag<T, OpR::kKMajor>(st + kOpBytes, rowb + 32 * j, s, lane);
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
+  };
+  if (nk > 0) issue(0);
+  phase_barrier<true, false>();                 // slice 0 resident
+  if (wave < kWaves / 2) {
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) issue(kt + 1);           // phase 2kt
+      read(kt);
+      phase_barrier<false, true>();
+      multiply();                               // phase 2kt + 1
+      phase_barrier<true, false>();
+    }
+    phase_barrier<false, false>();              // phase 2nk
+  } else {
+    if (1 < nk) issue(1);                       // phase 0
+    phase_barrier<false, false>();
+    for (int kt = 0; kt < nk; ++kt) {
+      read(kt);                                 // phase 2kt + 1
+      phase_barrier<true, true>();
+      if (kt + 2 < nk) issue(kt + 2);           // phase 2kt + 2
+      multiply();
+      phase_barrier<false, false>();
     }
   }
+  __syncthreads();   // LDS free for the epilogue
+}
+
+// The same product with both waves of a SIMD running the same interleaved stream of LDS reads
+// and MFMAs (one k-step's fragments live at a time: 24 registers instead of 96).  For kernels
+// whose other live state leaves no room for the ping-pong schedule's fragment registers.
+template <typename T, class OpC, class OpR>
+__device__ __forceinline__ void gemm_tile_interleaved(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C,
+                                                      const OpR& R, int k_begin, int k_end) {
+  static_assert(kStages == 2, "one slice in flight while the other is consumed");
+  constexpr int BK = slice_k<T>();
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rowb = (wave / kWaveCols) * 128;
+  const int colb = (wave % kWaveCols) * (kTile / kWaveCols);
+#pragma unroll
+  for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  if (nk > 0) {
+    C.issue(smem, k_begin, k_end, wave);
+    R.issue(smem + kOpBytes, k_begin, k_end, wave);
+  }
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's copies of slice kt have landed once at most the later slices' copies remain
-    // (then every wave's copies of slice kt are visible and slice kt-1 is consumed)
-    constexpr int kPer = 2 * kBlocksPerWave;   // copies per wave per slice
-    const int later = min(kStages - 2, nk - 1 - kt);
-    if (later >= 2) sync_slice<2 * kPer>();
-    else if (later == 1) sync_slice<kPer>();
-    else sync_slice<0>();
-    if (kt + kStages - 1 < nk) {
-      char* st = smem + ((kt + kStages - 1) % kStages) * kStageBytes;
-      const int k0 = k_begin + (kt + kStages - 1) * BK;
+    // slice kt landed (this wave's copies, then the barrier for everyone's); slice kt-1 consumed
+    phase_barrier<true, false>();
+    if (kt + 1 < nk) {
+      char* st = smem + ((kt + 1) % kStages) * kStageBytes;
+      const int k0 = k_begin + (kt + 1) * BK;
       C.issue(st, k0, k_end, wave);
       R.issue(st + kOpBytes, k0, k_end, wave);
     }

@@ -77,7 +77,7 @@ __device__ __forceinline__ void gemm_stream(f32x16 (&acc)[kColBlocks][4], char* 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   S.issue(ring, 0, k_end, wave);
   for (int kt = 0; kt < 8; ++kt) {
-    sync_slice<0>();
+    phase_barrier<true, false>();
     if (kt + 1 < 8) S.issue(ring + ((kt + 1) & 1) * kStreamBytes, (kt + 1) * 32, k_end, wave);
     const char* st = ring + (kt & 1) * kStreamBytes;
 #pragma unroll
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
     Operand<bf16_t, true> C, R;
     C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2), wave, lane);
     R.init(X, a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * 2), wave, lane);
-    gemm_tile<bf16_t>(acc, smem, C, R, 0, a.H);
+    gemm_tile_interleaved<bf16_t>(acc, smem, C, R, 0, a.H);
   }
 
   // 2. dlogits tile into LDS (bf16)
