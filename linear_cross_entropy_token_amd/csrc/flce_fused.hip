@@ -111,8 +111,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
   f32x16 acc[kColBlocks][4];
   {
     Operand<bf16_t, true> C, R;
-    C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2), wave, lane);
-    R.init(X, a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * 2), wave, lane);
+    C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2));
+    R.init(X, a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * 2));
     gemm_tile_interleaved<bf16_t>(acc, smem, C, R, 0, a.H);
   }
 
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
     const int h0 = hb * kTile;
     {
       Operand<bf16_t, false, kStreamBPW> S;           // W[n0 + v][h0 + h], contraction over v
-      S.init(W + (int64_t)n0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kv * a.H * 2), wave, lane);
+      S.init(W + (int64_t)n0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kv * a.H * 2));
       gemm_stream(acc, ring, S, kv, [&](int mnb, int ks, int ln) { return g_frag_k(g, mnb, ks, ln); });
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i) {
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
     }
     {
       Operand<bf16_t, false, kStreamBPW> S;           // x[m0 + token][h0 + h], contraction over tokens
-      S.init(X + (int64_t)m0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kt_ * a.H * 2), wave, lane);
+      S.init(X + (int64_t)m0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kt_ * a.H * 2));
       gemm_stream(acc, ring, S, kt_, [&](int mnb, int ks, int ln) { return g_frag_t(g, mnb, ks, ln); });
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i) {

@@ -36,9 +36,8 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   constexpr int ES = (int)sizeof(T);
 
   Operand<T, true> C, R;      // columns: W rows (vocab), rows: x rows (tokens)
-  C.init(static_cast<const T*>(a.W), a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
-  R.init(static_cast<const T*>(a.x), a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6,
-         tid & 63);
+  C.init(static_cast<const T*>(a.W), a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * ES));
+  R.init(static_cast<const T*>(a.x), a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * ES));
   f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, 0, a.H);
 
@@ -216,9 +215,8 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
 
   Operand<T, false> C;   // columns: W as [v][h] (hidden contiguous)
   Operand<T, true> R;    // rows: G as [token][v]
-  C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES), tid >> 6, tid & 63);
-  R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES), tid >> 6,
-         tid & 63);
+  C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES));
+  R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES));
   f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, ks, ke);
 
@@ -276,9 +274,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
 
   Operand<T, false> C;   // columns: x_c as [token][h]
   Operand<T, false> R;   // rows: G as [token][v]
-  C.init(static_cast<const T*>(a.x), a.H, n0, a.H, (uint32_t)((int64_t)a.rows * a.H * ES), tid >> 6, tid & 63);
-  R.init(static_cast<const T*>(a.g), a.ldg, m0, (int)a.ldg, (uint32_t)((int64_t)a.rows * a.ldg * ES),
-         tid >> 6, tid & 63);
+  C.init(static_cast<const T*>(a.x), a.H, n0, a.H, (uint32_t)((int64_t)a.rows * a.H * ES));
+  R.init(static_cast<const T*>(a.g), a.ldg, m0, (int)a.ldg, (uint32_t)((int64_t)a.rows * a.ldg * ES));
   f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, 0, a.rows);
 
