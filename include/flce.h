@@ -56,7 +56,9 @@ typedef enum {
                                  recomputes each logits tile, keeps its dlogits on chip and adds the
                                  dx / dW partials into fp32 accumulators with atomics.  bf16 inputs
                                  only.  With bf16 dW the accumulator is an extra V*H*4 bytes; with
-                                 fp32 dW it is dW itself.  Results are not bitwise repeatable. */
+                                 fp32 dW it is dW itself.  Results are not bitwise repeatable.
+                                 Size limit: (V + 256) * H * 4 and (chunk + 256) * H * 4 below
+                                 4 GiB (32-bit offsets into the accumulators), else UNSUPPORTED. */
 } flce_variant_t;
 
 typedef struct {

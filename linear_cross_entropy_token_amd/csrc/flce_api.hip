@@ -243,6 +243,10 @@ flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int
   const int64_t C = effective_chunk(N, H, V, chunk, es);
   const int64_t Vp = cdiv(V, kTile) * kTile;
   if (V * H * es >= lim || C * H * es >= lim || C * Vp * es >= lim) return FLCE_ERR_UNSUPPORTED;
+  // the fused variant adds into fp32 accumulators ([C, H] per chunk and [V, H]) through 32-bit
+  // buffer offsets, with up to one tile of rows past the end
+  if (cfg.variant == FLCE_FUSED && ((V + kTile) * H * 4 >= lim || (C + kTile) * H * 4 >= lim))
+    return FLCE_ERR_UNSUPPORTED;
   return FLCE_OK;
 }
 

@@ -95,6 +95,10 @@ extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
     i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds, int size, int voffset,
     int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+// No-return fp32 atomic add through a raw buffer (vector memory, added in L2).
+extern "C" __device__ float llvm_amdgcn_raw_buffer_atomic_fadd_f32(float v, i32x4 rsrc, int voffset, int soffset,
+                                                                   int aux) __asm("llvm.amdgcn.raw.buffer.atomic.fadd.f32");
+
 // Raw buffer over [base, base + bytes): reads at offsets >= bytes return zeros.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);

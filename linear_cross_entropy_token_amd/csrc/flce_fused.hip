@@ -153,22 +153,33 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
   char* ring = smem + kSmemBytes;
   const int kv = min(kTile, a.V - n0);      // valid vocabulary rows of the tile
   const int kt_ = min(kTile, a.rows - m0);  // valid token rows of the tile
+  const uint32_t row_bytes = (uint32_t)a.H * 4u;
+  const i32x4 dx_rsrc = make_rsrc(a.dx_acc, (uint32_t)((int64_t)a.rows * a.H * 4));
+  const i32x4 dw_rsrc = make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4));
   for (int hb = 0; hb < a.tiles_h; ++hb) {
     const int h0 = hb * kTile;
+    // Lane-dependent atomic offsets are formed here from an opaque copy of the lane id, so the
+    // compiler cannot hoist 128 of them over the loop; the per-register row offsets are
+    // wave-uniform and travel in the scalar offset.
+    int ol = lane;
+    asm volatile("" : "+v"(ol));
+    const int row_l = f.rowb + 4 * (ol >> 5);   // + 32 j + 8 (rg / 4) + rg % 4
     {
       Operand<bf16_t, false, kStreamBPW> S;           // W[n0 + v][h0 + h], contraction over v
       S.init(W + (int64_t)n0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)kv * a.H * 2));
       gemm_stream(acc, ring, S, kv, [&](int mnb, int ks, int ln) { return g_frag_k(g, mnb, ks, ln); });
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i) {
-        const int h = h0 + f.colb + 32 * i + (lane & 31);
+        const int h = h0 + f.colb + 32 * i + (ol & 31);
         if (h >= a.H) continue;
+        const uint32_t vbase = (uint32_t)(m0 + row_l) * row_bytes + (uint32_t)h * 4u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int rg = 0; rg < 16; ++rg) {
-            const int tok = m0 + f.rowb + 32 * j + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
-            if (tok < a.rows) unsafeAtomicAdd(a.dx_acc + (int64_t)tok * a.H + h, acc[i][j][rg]);
+            const int r = 32 * j + 8 * (rg >> 2) + (rg & 3);
+            if (m0 + row_l + r < a.rows)
+              llvm_amdgcn_raw_buffer_atomic_fadd_f32(acc[i][j][rg], dx_rsrc, (int)vbase, (int)((uint32_t)r * row_bytes), 0);
           }
       }
     }
@@ -178,14 +189,16 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
       gemm_stream(acc, ring, S, kt_, [&](int mnb, int ks, int ln) { return g_frag_t(g, mnb, ks, ln); });
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i) {
-        const int h = h0 + f.colb + 32 * i + (lane & 31);
+        const int h = h0 + f.colb + 32 * i + (ol & 31);
         if (h >= a.H) continue;
+        const uint32_t vbase = (uint32_t)(n0 + row_l) * row_bytes + (uint32_t)h * 4u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int rg = 0; rg < 16; ++rg) {
-            const int v = n0 + f.rowb + 32 * j + 8 * (rg >> 2) + 4 * (lane >> 5) + (rg & 3);
-            if (v < a.V) unsafeAtomicAdd(a.dw_acc + (int64_t)v * a.H + h, acc[i][j][rg]);
+            const int r = 32 * j + 8 * (rg >> 2) + (rg & 3);
+            if (n0 + row_l + r < a.V)
+              llvm_amdgcn_raw_buffer_atomic_fadd_f32(acc[i][j][rg], dw_rsrc, (int)vbase, (int)((uint32_t)r * row_bytes), 0);
           }
       }
     }
