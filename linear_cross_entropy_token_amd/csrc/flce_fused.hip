@@ -98,7 +98,7 @@ __device__ __forceinline__ void gemm_stream(f32x16 (&acc)[kColBlocks][4], char* 
 __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes + 2 * kStreamBytes];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
   const int tm = L % a.tiles_m;
   const int tn = L / a.tiles_m;

@@ -26,7 +26,8 @@ static_assert(kTile == kTileM && kTile == kTileN, "tile sizes of the dispatcher 
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  constexpr int kEpiBytes = 2 * kWaveCols * kTile * (int)sizeof(float) + kTile * (int)sizeof(int);
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes + kEpiBytes];
   const int tid = threadIdx.x;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
   int tm, tn;
@@ -38,74 +39,121 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   Operand<T, true> C, R;      // columns: W rows (vocab), rows: x rows (tokens)
   C.init(static_cast<const T*>(a.W), a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * ES));
   R.init(static_cast<const T*>(a.x), a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * ES));
+  // target column of each tile row (-1: not in this tile); loaded before the GEMM so its
+  // latency hides behind it
+  int rel = -1;
+  if (tid < kTile && m0 + tid < a.rows) {
+    const int64_t d = a.t[m0 + tid] - (int64_t)n0;
+    rel = (d >= 0 && d < kTile) ? (int)d : -1;
+  }
   f32x16 acc[kColBlocks][4];
   gemm_tile<T>(acc, smem, C, R, 0, a.H);
 
   const Frag f = frag_coords();
-  float* red = reinterpret_cast<float*>(smem);   // [2][kWaveCols][kTile]: per column-wave max, then sum
-  int* trel = reinterpret_cast<int*>(smem + 2 * kWaveCols * kTile * sizeof(float));
-  if (tid < kTile) {
-    const int r = m0 + tid;
-    int rel = -1;
-    if (r < a.rows) {
-      const int64_t d = a.t[r] - (int64_t)n0;
-      rel = (d >= 0 && d < kTile) ? (int)d : -1;
-    }
-    trel[tid] = rel;
-  }
-  __syncthreads();
+  // [2][kWaveCols][kTile]: per column-wave max, then sum; then the target column per row.  The
+  // ring below them holds the bf16 z tile (layout of the dW epilogue) on its way to HBM.
+  float* red = reinterpret_cast<float*>(smem + kSmemBytes);
+  int* trel = reinterpret_cast<int*>(smem + kSmemBytes + 2 * kWaveCols * kTile * sizeof(float));
+  if (tid < kTile) trel[tid] = rel;
+  phase_barrier<false, true>();
 
   const float ninf = -__builtin_inff();
   const int wc = (tid >> 6) % kWaveCols;
   const int vlim = a.V - n0;                // columns >= vlim are padding
+  const bool full = vlim >= kTile;          // wave-uniform: no padding column in this tile
   T* Z = static_cast<T*>(a.z);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = f.row(j);
     const int grow = m0 + row;
     float mx = ninf;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < kColBlocks; ++i)
+      for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-      for (int rg = 0; rg < 16; ++rg)
-        if (f.col0(i, rg >> 2) + (rg & 3) < vlim) mx = fmaxf(mx, acc[i][j][rg]);
+        for (int rg = 0; rg < 16; ++rg) mx = fmaxf(mx, acc[i][j][rg]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg)
+          if (f.col0(i, rg >> 2) + (rg & 3) < vlim) mx = fmaxf(mx, acc[i][j][rg]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // sum of exp(z - mx) as exp2(z log2 e - mx log2 e): one fma per element before the exp
+    const float mxl = mx * kLog2e;
     float s = 0.f;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < kColBlocks; ++i)
+      for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-      for (int rg = 0; rg < 16; ++rg)
-        if (f.col0(i, rg >> 2) + (rg & 3) < vlim) s += fast_exp(acc[i][j][rg] - mx);
+        for (int rg = 0; rg < 16; ++rg) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][rg], kLog2e, -mxl));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 16; ++rg)
+          if (f.col0(i, rg >> 2) + (rg & 3) < vlim)
+            s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][rg], kLog2e, -mxl));
+    }
     s += __shfl_xor(s, 32, 64);
     if (f.lane < 32) {
       red[wc * kTile + row] = mx;
       red[(kWaveCols + wc) * kTile + row] = s;
     }
     if (grow < a.rows) {
+      // the lane holding this row's target column (at most one per row) stores its logit;
+      // selected without branches
       const int tr = trel[row];
-      T* zrow = Z + (int64_t)grow * a.ldz + n0;
+      float zsel = 0.f;
+      bool hit = false;
 #pragma unroll
-      for (int i = 0; i < kColBlocks; ++i) {
+      for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c0 = f.col0(i, q);
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c0 + e == tr) a.zt[grow] = acc[i][j][4 * q + e];
-          if (Z == nullptr) continue;   // statistics-only pass
-          if constexpr (ES == 2) {
-            u32x2 v{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                    pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-            *reinterpret_cast<u32x2*>(zrow + c0) = v;
-          } else {
-            f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(zrow + c0) = v;
+          for (int e = 0; e < 4; ++e) {
+            const bool h = f.col0(i, q) + e == tr;
+            zsel = h ? acc[i][j][4 * q + e] : zsel;
+            hit = hit || h;
           }
-        }
+      if (hit) a.zt[grow] = zsel;
+      if (Z != nullptr) {   // null: statistics-only pass
+#pragma unroll
+        for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c0 = f.col0(i, q);
+            if constexpr (ES == 2) {
+              const int c = c0 >> 3;
+              *reinterpret_cast<u32x2*>(smem + row * 512 + ((c ^ (row & 31)) << 4) + 8 * (f.lane >> 5)) =
+                  u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            } else {
+              *reinterpret_cast<f32x4*>(Z + (int64_t)grow * a.ldz + n0 + c0) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
+          }
       }
     }
   }
-  __syncthreads();
+  phase_barrier<false, true>();   // partials and the z tile visible in LDS
+  if constexpr (ES == 2) {
+    if (Z != nullptr) {   // full 512-byte rows of z: 2 rows per 1 KiB block, 16 blocks per wave
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+      const int lane = tid & 63;
+      constexpr int kPerWave = kTile * kTile * 2 / 1024 / kWaves;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int b = wave * kPerWave + i;
+        const int r = 2 * b + (lane >> 5);
+        const int c = (lane & 31) ^ (r & 31);
+        if (m0 + r < a.rows)
+          *reinterpret_cast<u32x4*>(Z + (int64_t)(m0 + r) * a.ldz + n0 + 8 * c) =
+              *reinterpret_cast<const u32x4*>(smem + b * 1024 + 16 * lane);
+      }
+    }
+  }
   if (tid < kTile && m0 + tid < a.rows) {
     float M = ninf;
 #pragma unroll
@@ -201,7 +249,6 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int tid = threadIdx.x;
   const int tiles = a.tiles_m * a.tiles_n;
   const int L = xcd_remap(blockIdx.x, tiles * a.splits);
   const int split = L / tiles;
@@ -280,34 +327,76 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   gemm_tile<T>(acc, smem, C, R, 0, a.rows);
 
   const Frag f = frag_coords();
+  if (a.dw_fp32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = m0 + f.row(j);
+      if (v >= a.V) continue;
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int h = n0 + f.col0(i, q);
+          if (h >= a.H) continue;
+          f32x4 val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.dW) + (int64_t)v * a.H + h);
+          if (a.accumulate) val += *p;
+          *p = val;
+        }
+    }
+    return;
+  }
+  // bf16 dW: the 256 x 256 tile goes through the (now free) LDS ring as 256 rows of 512 bytes,
+  // 16-byte chunk c of row r at chunk c ^ (r % 32), so that HBM sees full-line copies (2 rows
+  // per 1 KiB copy) instead of 8-byte accesses that each touch 32 rows: the old tile comes in
+  // by direct-to-LDS copies, each lane adds its accumulators in place, full rows go out.
+  const i32x4 rs = make_rsrc(a.dW, (uint32_t)((int64_t)a.V * a.H * 2));
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  constexpr int kPerWave = kTile * kTile * 2 / 1024 / kWaves;
+  auto block_off = [&](int b, int& r) -> uint32_t {   // global byte offset of this lane's chunk
+    r = 2 * b + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 31);
+    const int v = m0 + r;
+    return (v < a.V && n0 + 8 * c < a.H) ? ((uint32_t)v * (uint32_t)a.H + (uint32_t)n0) * 2u + (uint32_t)c * 16u : kOOB;
+  };
+  if (a.accumulate) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      int r;
+      dma16(rs, smem + (wave * kPerWave + i) * 1024, block_off(wave * kPerWave + i, r));
+    }
+    phase_barrier<true, false>();
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int v = m0 + f.row(j);
-    if (v >= a.V) continue;
+    const int r = f.row(j);
 #pragma unroll
     for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int h = n0 + f.col0(i, q);
-        if (h >= a.H) continue;
+        const int c = f.col0(i, q) >> 3;
+        u32x2* s = reinterpret_cast<u32x2*>(smem + r * 512 + ((c ^ (r & 31)) << 4) + 8 * (f.lane >> 5));
         f32x4 val{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        const int64_t o = (int64_t)v * a.H + h;
-        if (a.dw_fp32) {
-          f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.dW) + o);
-          if (a.accumulate) val += *p;
-          *p = val;
-        } else {
-          u32x2* p = reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dW) + o);
-          if (a.accumulate) {
-            const u32x2 old = *p;
-            val[0] += bf16_to_f32(old[0] & 0xffffu);
-            val[1] += bf16_to_f32(old[0] >> 16);
-            val[2] += bf16_to_f32(old[1] & 0xffffu);
-            val[3] += bf16_to_f32(old[1] >> 16);
-          }
-          *p = u32x2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+        if (a.accumulate) {
+          const u32x2 old = *s;
+          val[0] += bf16_to_f32(old[0] & 0xffffu);
+          val[1] += bf16_to_f32(old[0] >> 16);
+          val[2] += bf16_to_f32(old[1] & 0xffffu);
+          val[3] += bf16_to_f32(old[1] >> 16);
         }
+        *s = u32x2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
       }
+  }
+  phase_barrier<false, true>();
+  bf16_t* dW = static_cast<bf16_t*>(a.dW);
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int b = wave * kPerWave + i;
+    int r;
+    const uint32_t off = block_off(b, r);
+    if (off != kOOB)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dW) + off) = *reinterpret_cast<const u32x4*>(smem + b * 1024 + 16 * lane);
   }
 }
 
