@@ -58,7 +58,6 @@ def measured_traffic(kernel: str, workload: str, chunk: int):
 
 def cpu_baseline(w, seconds_target: float = 15.0):
     """The CPU oracle (fp64, materialised logits) timed on a bounded token sample."""
-    import numpy as np
     import oracle
     from flce_inputs import make_inputs
     try:
@@ -66,25 +65,55 @@ def cpu_baseline(w, seconds_target: float = 15.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    n = 64
-    d = make_inputs(n, w.H, w.V, w.dtype, w.seed, w.targets)
-    x = oracle.widen(d["x"], w.dtype)
+    # Inputs are drawn once for the largest sample: seeded draws are prefix-stable in N, so the
+    # first n rows are exactly the workload's first n tokens.  Two small samples give the
+    # per-token cost without the fixed part (thread start-up); the timed sample is sized from it.
+    n_max = min(8192, w.N)
+    d = make_inputs(n_max, w.H, w.V, w.dtype, w.seed, w.targets)
+    x_all = oracle.widen(d["x"], w.dtype)
     W = oracle.widen(d["W"], w.dtype)
-    t0 = time.perf_counter()
-    oracle.flce(x, W, d["t"])
-    dt = time.perf_counter() - t0
-    n2 = int(min(8192, max(n, n * seconds_target / max(dt, 1e-3))))
-    n2 = max(n, (n2 // 64) * 64)
-    if n2 > n:
-        d = make_inputs(n2, w.H, w.V, w.dtype, w.seed, w.targets)
-        x = oracle.widen(d["x"], w.dtype)
+    t_all = d["t"]
+    del d
+
+    def run(n):
         t0 = time.perf_counter()
-        oracle.flce(x, W, d["t"])
-        dt = time.perf_counter() - t0
-        n = n2
+        oracle.flce(x_all[:n], W, t_all[:n])
+        return time.perf_counter() - t0
+
+    n_a, n_b = min(128, n_max), min(512, n_max)
+    c_a, c_b = run(n_a), run(n_b)
+    per_token = max((c_b - c_a) / max(n_b - n_a, 1), 1e-6)
+    n = max(n_b, min(n_max, int(seconds_target / per_token) // 64 * 64))
+    dt = run(n) if n > n_b else c_b
     return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} tokens of the {w.name} workload (full H={w.H}, V={w.V}), "
-                      f"fp64 NumPy oracle with materialised logits, {dt:.2f} s"}
+                      f"fp64 NumPy oracle with materialised logits, {dt:.2f} s",
+            "host": host_info()}
+
+
+def host_info():
+    """CPU model, BLAS library and host RAM of the machine the oracle ran on."""
+    info = {"cpu_model": None, "blas": None, "host_ram_gb": None}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:
+        pass
+    try:
+        info["host_ram_gb"] = round(os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES") / 1e9, 1)
+    except (ValueError, OSError):
+        pass
+    return info
 
 
 def materialised_peak(x, W, t):
@@ -177,15 +206,16 @@ def main():
         f.forward_backward(x, W, t, chunk=chunk, out=out)
     torch.cuda.synchronize()
     f.profile_enable(True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps (recorded on the stream, no host synchronisation)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         f.forward_backward(x, W, t, chunk=chunk, out=out)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     stats = f.profile_read()
     f.profile_enable(False)
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc + ws_bytes
@@ -219,7 +249,9 @@ def main():
                 "flops_per_launch": ds["flops"] / ds["launches"],
                 "avg_launch_ms": round(avg_s * 1e3, 4)}
 
-    extra = {"peak_extra_gb": round(peak_extra / 1e9, 3), "workspace_gb": round(ws_bytes / 1e9, 3),
+    extra = {"peak_extra_gb": round(peak_extra / 1e9, 3), "peak_extra_gib": round(peak_extra / 2**30, 3),
+             "dx_dtype": str(gdt).replace("torch.", ""), "dw_dtype": str(gdt).replace("torch.", ""),
+             "workspace_gb": round(ws_bytes / 1e9, 3),
              "free_delta_gb": round((free0 - free1) / 1e9, 3),
              "materialised_fp32_logits_gb": round(w.N * w.V * 4 / 1e9, 2)}
     if args.materialised:
@@ -245,6 +277,9 @@ def main():
     rec = {
         "metric": METRIC, "value": round(w.N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2] if len(step_ms) % 2
+                                    else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2]), 4),
+                    "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded x~N(0,1), W~N(0,0.02^2), targets "
                 + ("Zipf(1.1)" if w.targets == "zipf" else "uniform") + ")",
