@@ -148,6 +148,12 @@ def main():
     ap.add_argument("--variant", choices=["chunked", "fused"], default="chunked")
     ap.add_argument("--grad-dtype", choices=["input", "fp32"], default="input",
                     help="dtype of dx and dW (default: the input dtype)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="loss only (flce_forward_backward_opt with FLCE_FORWARD_ONLY); credited 2NHV flops")
+    ap.add_argument("--reduction", choices=["mean", "sum"], default="mean")
+    ap.add_argument("--ignore-frac", type=float, default=0.0,
+                    help="set this fraction of the targets (seeded) to -100 and pass ignore_index=-100")
+    ap.add_argument("--accumulate", action="store_true", help="add the gradients into dx and dW")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="also measure the peak HBM of the materialised-logits PyTorch path")
@@ -181,8 +187,14 @@ def main():
     else:
         x = torch.from_numpy(d["x"]).to(dev)
         W = torch.from_numpy(d["W"]).to(dev)
+    if args.ignore_frac > 0:
+        rng = np.random.default_rng(w.seed + 7919)
+        d["t"] = np.where(rng.random(w.N) < args.ignore_frac, -100, d["t"])
     t = torch.from_numpy(d["t"]).to(dev)
     del d
+    ignore = -100 if args.ignore_frac > 0 else None
+    if args.forward_only and args.accumulate:
+        raise SystemExit("--forward-only and --accumulate exclude each other")
     log(f"[bench] inputs on device in {time.perf_counter() - t0:.1f} s")
 
     torch.cuda.synchronize()
@@ -195,15 +207,26 @@ def main():
     dW = torch.empty(W.shape, dtype=gdt, device=dev)
     base_alloc = torch.cuda.memory_allocated()
     free0, _ = torch.cuda.mem_get_info()
-    f.reserve(w.N, w.H, w.V, chunk)
+    if not args.forward_only:   # a forward-only call sizes its (smaller) workspace itself
+        f.reserve(w.N, w.H, w.V, chunk)
     free1, total_mem = torch.cuda.mem_get_info()
-    ws_bytes = f.workspace_bytes(w.N, w.H, w.V, chunk)
+    ws_bytes = f.workspace_bytes(w.N, w.H, w.V, chunk, forward_only=args.forward_only)
     eff_chunk = flce.flce_effective_chunk(w.N, w.H, w.V, chunk)
 
     out = (loss, dx, dW, None)
     stream = torch.cuda.current_stream(dev)
+    if args.accumulate:
+        dx.zero_()
+        dW.zero_()
+
+    def step():
+        if args.forward_only:
+            return f.forward(x, W, t, chunk=chunk, reduction=args.reduction, ignore_index=ignore)
+        return f.forward_backward(x, W, t, chunk=chunk, out=out, reduction=args.reduction, ignore_index=ignore,
+                                  accumulate=args.accumulate)
+
     for _ in range(args.warmup):
-        f.forward_backward(x, W, t, chunk=chunk, out=out)
+        step()
     torch.cuda.synchronize()
     f.profile_enable(True)
     # one event between consecutive steps (recorded on the stream, no host synchronisation)
@@ -211,20 +234,22 @@ def main():
     torch.cuda.synchronize()
     evs[0].record(stream)
     for i in range(args.steps):
-        f.forward_backward(x, W, t, chunk=chunk, out=out)
+        res = step()
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = evs[0].elapsed_time(evs[-1]) / args.steps
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     stats = f.profile_read()
     f.profile_enable(False)
+    if args.forward_only:
+        loss = res
     peak_extra = torch.cuda.max_memory_allocated() - base_alloc + ws_bytes
     status = f.check()
     log(f"[bench] {ms:.3f} ms/step, loss {loss.item():.6f}, check status {status}")
     if status != 0 or not math.isfinite(loss.item()):
         raise SystemExit(f"bench run is invalid: status {status}, loss {loss.item()}")
 
-    flops_step = 6.0 * w.N * w.H * w.V
+    flops_step = (2.0 if args.forward_only else 6.0) * w.N * w.H * w.V
     tflops = flops_step / (ms * 1e-3) / 1e12
     peak_tf = PEAK_TFLOPS[w.dtype]
     kernels = {}
@@ -286,7 +311,9 @@ def main():
         "config": {"workload": f"{w.name}: N={w.N} H={w.H} V={w.V} {w.dtype}, chunk {eff_chunk}",
                    "N": w.N, "H": w.H, "V": w.V, "chunk": eff_chunk, "variant": args.variant,
                    "grad_dtype": "fp32" if args.grad_dtype == "fp32" else w.dtype,
-                   "parallelism": "single GPU"},
+                   "mode": "forward" if args.forward_only else "forward+backward",
+                   "reduction": args.reduction, "ignore_frac": args.ignore_frac,
+                   "accumulate": args.accumulate, "parallelism": "single GPU"},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
     }

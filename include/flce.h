@@ -105,6 +105,46 @@ flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const voi
                                        int64_t chunk, float* loss, void* dx, void* dW, float* lse,
                                        void* stream);
 
+/* Options of flce_forward_backward_opt: the loss reduction, masked tokens, accumulation into
+ * the gradient outputs, and a forward-only (loss) mode.  These are the conventions of PyTorch's
+ * cross_entropy(reduction=..., ignore_index=...); the FLCE page's interface fixes none of them
+ * (its listing is the mean over all tokens, overwriting dx and dW, which is the default). */
+typedef enum {
+  FLCE_MEAN = 0,              /* loss and gradients divided by the number of counted tokens */
+  FLCE_SUM = 1                /* not divided */
+} flce_reduction_t;
+
+enum {
+  FLCE_ACCUMULATE = 1,        /* dx += d loss / d x and dW += d loss / d W (sum in fp32, one rounding
+                                 to the output dtype per call); default: overwrite */
+  FLCE_FORWARD_ONLY = 2       /* loss (and lse) only: dx, dW are not touched and may be NULL, and the
+                                 chunked variant needs no logits buffer */
+};
+
+typedef struct {
+  int32_t reduction;          /* flce_reduction_t */
+  int32_t flags;              /* FLCE_ACCUMULATE | FLCE_FORWARD_ONLY (not both) */
+  int32_t ignore_on;          /* 1: tokens whose target equals ignore_index count for nothing: no loss,
+                                 a zero gradient row, not in the mean's denominator.  A mean over
+                                 zero counted tokens is NaN (0/0) with zero gradients. */
+  int32_t reserved;           /* must be 0 */
+  int64_t ignore_index;       /* e.g. -100; any value, inside [0, V) or not */
+} flce_options_t;
+
+/* flce_forward_backward_ex with options; opt == NULL gives the defaults (mean, overwrite, no
+ * ignored tokens, gradients).  The count of counted tokens is taken on the device.
+ * Errors: as flce_forward_backward, and INVALID_ARG for an unknown reduction or flag, both
+ * flags at once, ignore_on outside {0, 1}, reserved != 0, or NULL dx / dW with gradients. */
+flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const void* W,
+                                        const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                        int64_t chunk, const flce_options_t* opt, float* loss, void* dx,
+                                        void* dW, float* lse, void* stream);
+
+/* Workspace bytes a flce_forward_backward_opt call with these sizes and options needs (0 for
+ * invalid sizes or options); forward only needs no logits buffer and no gradient accumulators. */
+size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                const flce_options_t* opt);
+
 /* Token chunk the call would use (for bf16 inputs): chunk clamped to [1, N] when positive; for
  * chunk <= 0 the size rule of the FLCE page's trade-offs section, next_pow2(ceil(N / ceil(V/H))),
  * raised to at least 4096 tokens (on MI355X the chunk's GEMMs run faster with the longer token

@@ -18,13 +18,16 @@ from typing import Optional
 __all__ = [
     "FLCE_BF16", "FLCE_FP32", "FLCE_CHUNKED", "FLCE_FUSED", "STATUS", "FlceError", "Config",
     "library_path", "load_library", "flce_create", "flce_destroy", "flce_forward_backward",
-    "flce_forward_backward_ex", "flce_effective_chunk", "flce_workspace_bytes", "flce_reserve",
+    "flce_forward_backward_ex", "flce_forward_backward_opt", "Options", "FLCE_MEAN", "FLCE_SUM",
+    "FLCE_ACCUMULATE", "FLCE_FORWARD_ONLY", "flce_effective_chunk", "flce_workspace_bytes", "flce_workspace_bytes_opt", "flce_reserve",
     "flce_check", "flce_status_string", "flce_profile_enable", "flce_profile_read", "KernelStat",
     "FusedLinearCrossEntropy",
 ]
 
 FLCE_BF16, FLCE_FP32 = 0, 1
 FLCE_CHUNKED, FLCE_FUSED = 0, 1
+FLCE_MEAN, FLCE_SUM = 0, 1
+FLCE_ACCUMULATE, FLCE_FORWARD_ONLY = 1, 2
 STATUS = {0: "FLCE_OK", 1: "FLCE_ERR_INVALID_ARG", 2: "FLCE_ERR_UNSUPPORTED", 3: "FLCE_ERR_OOM",
           4: "FLCE_ERR_HIP", 5: "FLCE_ERR_DATA"}
 
@@ -40,6 +43,11 @@ class Config(ctypes.Structure):
                 ("dw_dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("workspace_limit", ctypes.c_int64)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("reduction", ctypes.c_int32), ("flags", ctypes.c_int32), ("ignore_on", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("ignore_index", ctypes.c_int64)]
 
 
 class KernelStat(ctypes.Structure):
@@ -72,10 +80,15 @@ def load_library() -> ctypes.CDLL:
     lib.flce_forward_backward.restype = i32
     lib.flce_forward_backward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.flce_forward_backward_ex.restype = i32
+    lib.flce_forward_backward_opt.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(Options),
+                                              vp, vp, vp, vp, vp]
+    lib.flce_forward_backward_opt.restype = i32
     lib.flce_effective_chunk.argtypes = [i64, i64, i64, i64]
     lib.flce_effective_chunk.restype = i64
     lib.flce_workspace_bytes.argtypes = [vp, i64, i64, i64, i64]
     lib.flce_workspace_bytes.restype = ctypes.c_size_t
+    lib.flce_workspace_bytes_opt.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(Options)]
+    lib.flce_workspace_bytes_opt.restype = ctypes.c_size_t
     lib.flce_reserve.argtypes = [vp, i64, i64, i64, i64]
     lib.flce_reserve.restype = i32
     lib.flce_check.argtypes = [vp, vp]
@@ -117,12 +130,24 @@ def flce_forward_backward_ex(handle, x, W, targets, N, H, V, chunk, loss, dx, dW
                                                    lse, stream)
 
 
+def flce_forward_backward_opt(handle, x, W, targets, N, H, V, chunk, opt, loss, dx, dW, lse, stream) -> int:
+    """opt: an Options instance or None (defaults)."""
+    return load_library().flce_forward_backward_opt(handle, x, W, targets, N, H, V, chunk,
+                                                    ctypes.byref(opt) if opt is not None else None,
+                                                    loss, dx, dW, lse, stream)
+
+
 def flce_effective_chunk(N, H, V, chunk) -> int:
     return load_library().flce_effective_chunk(N, H, V, chunk)
 
 
 def flce_workspace_bytes(handle, N, H, V, chunk) -> int:
     return load_library().flce_workspace_bytes(handle, N, H, V, chunk)
+
+
+def flce_workspace_bytes_opt(handle, N, H, V, chunk, opt) -> int:
+    return load_library().flce_workspace_bytes_opt(handle, N, H, V, chunk,
+                                                   ctypes.byref(opt) if opt is not None else None)
 
 
 def flce_reserve(handle, N, H, V, chunk) -> int:
@@ -192,7 +217,9 @@ class FusedLinearCrossEntropy:
         except Exception:
             pass
 
-    def workspace_bytes(self, N, H, V, chunk=0) -> int:
+    def workspace_bytes(self, N, H, V, chunk=0, forward_only: bool = False) -> int:
+        if forward_only:
+            return flce_workspace_bytes_opt(self.handle, N, H, V, chunk, _options("mean", None, FLCE_FORWARD_ONLY))
         return flce_workspace_bytes(self.handle, N, H, V, chunk)
 
     def reserve(self, N, H, V, chunk=0):
@@ -216,11 +243,18 @@ class FusedLinearCrossEntropy:
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         return flce_check(self.handle, s.cuda_stream)
 
-    def forward_backward(self, x, W, t, chunk: int = 0, with_lse: bool = False, out=None, stream=None):
+    def forward_backward(self, x, W, t, chunk: int = 0, with_lse: bool = False, out=None, stream=None,
+                         reduction: str = "mean", ignore_index: Optional[int] = None,
+                         accumulate: bool = False):
+        """Loss and both gradients.  ``reduction`` is "mean" (over tokens whose target is not
+        ``ignore_index``) or "sum"; with ``accumulate`` the gradients are added into the ``dx``
+        and ``dW`` of ``out`` instead of overwriting them."""
         import torch
         N, H = x.shape
         V = W.shape[0]
         if out is None:
+            if accumulate:
+                raise ValueError("accumulate needs the dx and dW to add into (out=...)")
             loss = torch.empty((), dtype=torch.float32, device=x.device)
             dx = torch.empty((N, H), dtype=self.dx_dtype, device=x.device)
             dW = torch.empty((V, H), dtype=self.dw_dtype, device=x.device)
@@ -233,9 +267,39 @@ class FusedLinearCrossEntropy:
         if x.dtype != self.in_dtype or W.dtype != self.in_dtype or t.dtype != torch.int64:
             raise ValueError("dtype mismatch with the handle's configuration")
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
-        st = flce_forward_backward_ex(self.handle, x.data_ptr(), W.data_ptr(), t.data_ptr(), N, H, V,
-                                      chunk, loss.data_ptr(), dx.data_ptr(), dW.data_ptr(),
-                                      lse.data_ptr() if lse is not None else None, s.cuda_stream)
+        opt = _options(reduction, ignore_index, FLCE_ACCUMULATE if accumulate else 0)
+        st = flce_forward_backward_opt(self.handle, x.data_ptr(), W.data_ptr(), t.data_ptr(), N, H, V,
+                                       chunk, opt, loss.data_ptr(), dx.data_ptr(), dW.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, s.cuda_stream)
         if st != 0:
             raise FlceError(st, "flce_forward_backward")
         return (loss, dx, dW, lse) if with_lse else (loss, dx, dW)
+
+    def forward(self, x, W, t, chunk: int = 0, with_lse: bool = False, stream=None,
+                reduction: str = "mean", ignore_index: Optional[int] = None):
+        """Loss only (and the per-token log-sum-exp if asked); no gradient is computed."""
+        import torch
+        N, H = x.shape
+        V = W.shape[0]
+        for name, ten in (("x", x), ("W", W), ("targets", t)):
+            if not ten.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if x.dtype != self.in_dtype or W.dtype != self.in_dtype or t.dtype != torch.int64:
+            raise ValueError("dtype mismatch with the handle's configuration")
+        loss = torch.empty((), dtype=torch.float32, device=x.device)
+        lse = torch.empty((N,), dtype=torch.float32, device=x.device) if with_lse else None
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        opt = _options(reduction, ignore_index, FLCE_FORWARD_ONLY)
+        st = flce_forward_backward_opt(self.handle, x.data_ptr(), W.data_ptr(), t.data_ptr(), N, H, V,
+                                       chunk, opt, loss.data_ptr(), None, None,
+                                       lse.data_ptr() if lse is not None else None, s.cuda_stream)
+        if st != 0:
+            raise FlceError(st, "flce_forward_backward_opt")
+        return (loss, lse) if with_lse else loss
+
+
+def _options(reduction: str, ignore_index: Optional[int], flags: int) -> Options:
+    if reduction not in ("mean", "sum"):
+        raise ValueError(f"reduction must be 'mean' or 'sum', not {reduction!r}")
+    return Options(FLCE_SUM if reduction == "sum" else FLCE_MEAN, flags, 0 if ignore_index is None else 1, 0,
+                   0 if ignore_index is None else int(ignore_index))

@@ -37,8 +37,18 @@ struct Plan {
   int64_t k_per_split = 0;
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
+  size_t off_scale = 0;                  // flce::Scale of the call
   bool fused = false;
+  bool grads = true;                     // false: forward only (no logits buffer, no accumulators)
   size_t total = 0;
+};
+
+// Per-call options in the form the launch sequence uses.
+struct Opts {
+  flce::Ignore ign{0, 0};
+  int sum = 0;
+  bool accumulate = false;
+  bool grads = true;
 };
 
 }  // namespace
@@ -46,10 +56,12 @@ struct Plan {
 namespace {
 
 enum Kernel {
-  K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_FUSED_BWD, K_FILL, K_CAST, K_COUNT
+  K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_FUSED_BWD, K_FILL, K_CAST,
+  K_SCALE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"logits_lse", "lse_combine", "dlogits", "dx", "dx_reduce",
-                                           "dw", "finalize", "fused_bwd", "fill_zero", "cast_bf16"};
+                                           "dw", "finalize", "fused_bwd", "fill_zero", "cast_bf16",
+                                           "scale"};
 
 struct Mark {
   int kind;                 // Kernel, or -1 for the event that closes a call
@@ -167,7 +179,7 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
-Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk) {
+Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true) {
   Plan p;
   p.N = N;
   p.H = H;
@@ -187,20 +199,23 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.k_per_split = cdiv(cdiv(p.Vp, s), bk) * bk;
 
   p.fused = cfg.variant == FLCE_FUSED;
+  p.grads = grads;
   size_t off = 0;
+  p.off_scale = off;
+  off = align_up(off + sizeof(flce::Scale));
   p.off_z = off;
-  if (!p.fused) off = align_up(off + (size_t)p.C * p.Vp * in_size(cfg));
+  if (!p.fused && grads) off = align_up(off + (size_t)p.C * p.Vp * in_size(cfg));
   p.off_pm = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
   p.off_ps = off;   off = align_up(off + (size_t)p.tiles_v * p.C * sizeof(float));
   p.off_zt = off;   off = align_up(off + (size_t)N * sizeof(float));
   p.off_lse = off;  off = align_up(off + (size_t)N * sizeof(float));
   p.off_loss = off; off = align_up(off + (size_t)N * sizeof(float));
   p.off_part = off;
-  if (!p.fused && p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
+  if (!p.fused && grads && p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
   p.off_dxacc = off;
-  if (p.fused && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
+  if (p.fused && grads && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
   p.off_dwacc = off;
-  if (p.fused && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
+  if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
   p.total = off;
   return p;
 }
@@ -255,7 +270,20 @@ flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int
     if ((call) != hipSuccess) return FLCE_ERR_HIP; \
   } while (0)
 
-flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const void* W,
+// Token count and normalisation of the call, on the device (no host synchronisation).
+flce_status_t launch_scale(flce_handle_s* h, const Plan& p, const Opts& o, const int64_t* t, hipStream_t st) {
+  flce::ScaleArgs sa{};
+  sa.t = t;
+  sa.n = p.N;
+  sa.ign = o.ign;
+  sa.sum = o.sum;
+  sa.out = reinterpret_cast<flce::Scale*>(static_cast<char*>(h->ws) + p.off_scale);
+  FLCE_LAUNCH(mark(h, K_SCALE, 0.0, 8.0 * p.N, st));
+  FLCE_LAUNCH(flce::launch_scale(sa, st));
+  return FLCE_OK;
+}
+
+flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
                           const int64_t* t, float* loss, void* dx, void* dW, float* lse_out,
                           hipStream_t st) {
   const flce_config_t& cfg = h->cfg;
@@ -270,22 +298,24 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
   float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
   const size_t dx_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
-  const float inv_n = (float)(1.0 / (double)p.N);
+  const flce::Scale* scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
   const double b_in = (double)es, b_dx = (double)dx_es;
   const double b_dw = cfg.dw_dtype == FLCE_BF16 ? 2.0 : 4.0;
   const double VH = (double)p.V * (double)p.H;
+  const flce_status_t sc = launch_scale(h, p, o, t, st);
+  if (sc != FLCE_OK) return sc;
 
   for (int64_t s = 0; s < p.N; s += p.C) {
     const int rows = (int)std::min(p.C, p.N - s);
     const int tiles_m = (int)cdiv(rows, kTile);
     const double gemm_flops = 2.0 * rows * VH;
-    const double zbytes = (double)rows * (double)p.V * b_in;
+    const double zbytes = o.grads ? (double)rows * (double)p.V * b_in : 0.0;
 
     flce::LogitsArgs la{};
     la.x = static_cast<const char*>(x) + (size_t)s * p.H * es;
     la.W = W;
     la.t = t + s;
-    la.z = z;
+    la.z = o.grads ? z : nullptr;   // forward only: statistics, no logits buffer
     la.pm = pm;
     la.ps = ps;
     la.zt = zt + s;
@@ -307,12 +337,14 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
     ca.lse = lse + s;
     ca.loss_rows = loss_rows + s;
     ca.flag = h->flag;
+    ca.ign = o.ign;
     ca.pstride = (int)p.C;
     ca.tiles_n = p.tiles_v;
     ca.rows = rows;
     ca.V = (int)p.V;
     FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
     FLCE_LAUNCH(flce::launch_combine(ca, st));
+    if (!o.grads) continue;
 
     flce::DlogitsArgs ga{};
     ga.z = z;
@@ -321,7 +353,8 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
     ga.ldz = p.Vp;
     ga.rows = rows;
     ga.V = (int)p.V;
-    ga.inv_n = inv_n;
+    ga.ign = o.ign;
+    ga.scale = scale;
     FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes, st));
     FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
 
@@ -340,6 +373,7 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
     xa.tiles_m = tiles_m;
     xa.tiles_n = p.tiles_h;
     xa.dx_fp32 = cfg.dx_dtype == FLCE_FP32;
+    xa.accumulate = o.accumulate;
     FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
     FLCE_LAUNCH(flce::launch_dx(in, xa, st));
     if (p.splits > 1) {
@@ -350,6 +384,7 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
       ra.count = (int64_t)rows * p.H;
       ra.splits = p.splits;
       ra.dx_fp32 = xa.dx_fp32;
+      ra.accumulate = o.accumulate;
       FLCE_LAUNCH(mark(h, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
       FLCE_LAUNCH(flce::launch_dx_reduce(ra, st));
     }
@@ -365,9 +400,9 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
     wa.tiles_m = p.tiles_v;
     wa.tiles_n = p.tiles_h;
     wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
-    wa.accumulate = s > 0;
+    wa.accumulate = s > 0 || o.accumulate;
     FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
-                     zbytes + (double)rows * p.H * b_in + VH * b_dw * (s > 0 ? 2.0 : 1.0), st));
+                     zbytes + (double)rows * p.H * b_in + VH * b_dw * (wa.accumulate ? 2.0 : 1.0), st));
     FLCE_LAUNCH(flce::launch_dw(in, wa, st));
   }
 
@@ -375,6 +410,7 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
   fa.loss_rows = loss_rows;
   fa.loss = loss;
   fa.n = p.N;
+  fa.scale = scale;
   FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
   FLCE_LAUNCH(flce::launch_finalize(fa, st));
   FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
@@ -383,8 +419,8 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const void* x, const 
 
 // Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and pass 2
 // (recompute, dlogits in LDS, dx and dW partials by fp32 atomics); outputs converted last.
-flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const void* W, const int64_t* t,
-                        float* loss, void* dx, void* dW, float* lse_out, hipStream_t st) {
+flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
+                        const int64_t* t, float* loss, void* dx, void* dW, float* lse_out, hipStream_t st) {
   const flce_config_t& cfg = h->cfg;
   char* ws = static_cast<char*>(h->ws);
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
@@ -394,12 +430,17 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const vo
   float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   const bool dx32 = cfg.dx_dtype == FLCE_FP32, dw32 = cfg.dw_dtype == FLCE_FP32;
   float* dw_acc = dw32 ? static_cast<float*>(dW) : reinterpret_cast<float*>(ws + p.off_dwacc);
-  const float inv_n = (float)(1.0 / (double)p.N);
+  const flce::Scale* scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
   const double VH = (double)p.V * (double)p.H;
+  const flce_status_t sc = launch_scale(h, p, o, t, st);
+  if (sc != FLCE_OK) return sc;
 
-  flce::FillArgs zw{dw_acc, p.V * p.H};
-  FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * VH, st));
-  FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
+  // fp32 outputs are the accumulators themselves: cleared unless the call accumulates into them
+  if (o.grads && !(dw32 && o.accumulate)) {
+    flce::FillArgs zw{dw_acc, p.V * p.H};
+    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * VH, st));
+    FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
+  }
   for (int64_t s = 0; s < p.N; s += p.C) {
     const int rows = (int)std::min(p.C, p.N - s);
     const int tiles_m = (int)cdiv(rows, kTile);
@@ -432,17 +473,21 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const vo
     ca.lse = lse + s;
     ca.loss_rows = loss_rows + s;
     ca.flag = h->flag;
+    ca.ign = o.ign;
     ca.pstride = (int)p.C;
     ca.tiles_n = p.tiles_v;
     ca.rows = rows;
     ca.V = (int)p.V;
     FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
     FLCE_LAUNCH(flce::launch_combine(ca, st));
+    if (!o.grads) continue;
 
     float* dx_acc = dx32 ? static_cast<float*>(dx) + (size_t)s * p.H : reinterpret_cast<float*>(ws + p.off_dxacc);
-    flce::FillArgs zx{dx_acc, (int64_t)rows * p.H};
-    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * rows * p.H, st));
-    FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
+    if (!(dx32 && o.accumulate)) {
+      flce::FillArgs zx{dx_acc, (int64_t)rows * p.H};
+      FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * rows * p.H, st));
+      FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
+    }
 
     flce::FusedArgs fa{};
     fa.x = xs;
@@ -457,18 +502,19 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const vo
     fa.tiles_m = tiles_m;
     fa.tiles_n = p.tiles_v;
     fa.tiles_h = p.tiles_h;
-    fa.inv_n = inv_n;
+    fa.ign = o.ign;
+    fa.scale = scale;
     // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
     FLCE_LAUNCH(mark(h, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
     FLCE_LAUNCH(flce::launch_fused_bwd(fa, st));
     if (!dx32) {
-      flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H};
+      flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
       FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_cast_bf16(cx, st));
     }
   }
-  if (!dw32) {
-    flce::CastArgs cw{dw_acc, dW, p.V * p.H};
+  if (o.grads && !dw32) {
+    flce::CastArgs cw{dw_acc, dW, p.V * p.H, o.accumulate};
     FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * VH, st));
     FLCE_LAUNCH(flce::launch_cast_bf16(cw, st));
   }
@@ -476,6 +522,7 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const void* x, const vo
   fa.loss_rows = loss_rows;
   fa.loss = loss;
   fa.n = p.N;
+  fa.scale = scale;
   FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
   FLCE_LAUNCH(flce::launch_finalize(fa, st));
   FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
@@ -541,6 +588,17 @@ size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, in
   return make_plan(h->cfg, N, H, V, chunk).total;
 }
 
+size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                const flce_options_t* opt) {
+  if (h == nullptr || validate_sizes(h->cfg, N, H, V, chunk) != FLCE_OK) return 0;
+  bool grads = true;
+  if (opt != nullptr) {
+    if ((opt->flags & ~(FLCE_ACCUMULATE | FLCE_FORWARD_ONLY)) != 0) return 0;
+    grads = (opt->flags & FLCE_FORWARD_ONLY) == 0;
+  }
+  return make_plan(h->cfg, N, H, V, chunk, grads).total;
+}
+
 flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
   if (h == nullptr) return FLCE_ERR_INVALID_ARG;
   const flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
@@ -548,33 +606,53 @@ flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int
   return ensure_workspace(h, make_plan(h->cfg, N, H, V, chunk).total);
 }
 
-flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,
-                                       const int64_t* targets, int64_t N, int64_t H, int64_t V,
-                                       int64_t chunk, float* loss, void* dx, void* dW, float* lse,
-                                       void* stream) {
+flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const void* W,
+                                        const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                        int64_t chunk, const flce_options_t* opt, float* loss, void* dx,
+                                        void* dW, float* lse, void* stream) {
+  Opts o;
+  if (opt != nullptr) {
+    if ((opt->reduction != FLCE_MEAN && opt->reduction != FLCE_SUM) ||
+        (opt->flags & ~(FLCE_ACCUMULATE | FLCE_FORWARD_ONLY)) != 0 ||
+        ((opt->flags & FLCE_ACCUMULATE) && (opt->flags & FLCE_FORWARD_ONLY)) || opt->ignore_on < 0 ||
+        opt->ignore_on > 1 || opt->reserved != 0)
+      return FLCE_ERR_INVALID_ARG;
+    o.sum = opt->reduction == FLCE_SUM;
+    o.accumulate = (opt->flags & FLCE_ACCUMULATE) != 0;
+    o.grads = (opt->flags & FLCE_FORWARD_ONLY) == 0;
+    o.ign = flce::Ignore{opt->ignore_index, opt->ignore_on};
+  }
   if (h == nullptr || x == nullptr || W == nullptr || targets == nullptr || loss == nullptr ||
-      dx == nullptr || dW == nullptr)
+      (o.grads && (dx == nullptr || dW == nullptr)))
     return FLCE_ERR_INVALID_ARG;
   const flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
   if (v != FLCE_OK) return v;
-  if (!aligned16(x) || !aligned16(W) || !aligned16(dx) || !aligned16(dW) ||
+  if (!aligned16(x) || !aligned16(W) || (o.grads && (!aligned16(dx) || !aligned16(dW))) ||
       (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return FLCE_ERR_UNSUPPORTED;
-  if (dx == x || dW == W) return FLCE_ERR_INVALID_ARG;
-  const Plan p = make_plan(h->cfg, N, H, V, chunk);
+  if (o.grads && (dx == x || dW == W)) return FLCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads);
   const flce_status_t ws = ensure_workspace(h, p.total);
   if (ws != FLCE_OK) return ws;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
-  if (p.fused) return run_fused(h, p, x, W, targets, loss, dx, dW, lse, static_cast<hipStream_t>(stream));
-  return run_chunked(h, p, x, W, targets, loss, dx, dW, lse, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.fused) return run_fused(h, p, o, x, W, targets, loss, dx, dW, lse, st);
+  return run_chunked(h, p, o, x, W, targets, loss, dx, dW, lse, st);
+}
+
+flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,
+                                       const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                       int64_t chunk, float* loss, void* dx, void* dW, float* lse,
+                                       void* stream) {
+  return flce_forward_backward_opt(h, x, W, targets, N, H, V, chunk, nullptr, loss, dx, dW, lse, stream);
 }
 
 flce_status_t flce_forward_backward(flce_handle_t h, const void* x, const void* W,
                                     const int64_t* targets, int64_t N, int64_t H, int64_t V,
                                     int64_t chunk, float* loss, void* dx, void* dW, void* stream) {
-  return flce_forward_backward_ex(h, x, W, targets, N, H, V, chunk, loss, dx, dW, nullptr, stream);
+  return flce_forward_backward_opt(h, x, W, targets, N, H, V, chunk, nullptr, loss, dx, dW, nullptr, stream);
 }
 
 flce_status_t flce_profile_enable(flce_handle_t h, int enable) {

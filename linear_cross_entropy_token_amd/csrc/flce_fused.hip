@@ -118,14 +118,15 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
 
   // 2. dlogits tile into LDS (bf16)
   char* g = smem;
+  const float gscale = a.scale->grad;
   const Frag f = frag_coords();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = f.row(j);
     const int tok = m0 + row;
-    const bool rok = tok < a.rows;
+    const int64_t tv = tok < a.rows ? a.t[tok] : -1;
+    const bool rok = tok < a.rows && !a.ign.skip(tv);   // an ignored token's row of G is zero
     const float l = rok ? a.lse[tok] : 0.f;
-    const int64_t tv = rok ? a.t[tok] : -1;
 #pragma unroll
     for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_bwd_kernel(FusedArgs a) {
           if (rok && v < a.V) {
             x = fast_exp(acc[i][j][4 * q + e] - l);
             if (v == tv) x -= 1.f;
-            x *= a.inv_n;
+            x *= gscale;
           }
           gv[e] = x;
         }
@@ -214,9 +215,16 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(FillArgs a) {
 __global__ __launch_bounds__(256) void cast_bf16_kernel(CastArgs a) {
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < a.n;
        i += (int64_t)gridDim.x * blockDim.x * 4) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.src + i);
-    *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dst) + i) =
-        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    f32x4 v = *reinterpret_cast<const f32x4*>(a.src + i);
+    u32x2* p = reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dst) + i);
+    if (a.accumulate) {
+      const u32x2 old = *p;
+      v[0] += bf16_to_f32(old[0] & 0xffffu);
+      v[1] += bf16_to_f32(old[0] >> 16);
+      v[2] += bf16_to_f32(old[1] & 0xffffu);
+      v[3] += bf16_to_f32(old[1] >> 16);
+    }
+    *p = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
 }
 

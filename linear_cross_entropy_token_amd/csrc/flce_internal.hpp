@@ -12,6 +12,31 @@ constexpr int kSliceBytesABI = 128; // bytes of contraction per operand row and 
 // Element type of x and W (and of the chunk's logits/dlogits buffer).
 enum class In { BF16 = 0, FP32 = 1 };
 
+// Per-call normalisation, written on the device by the scale kernel before anything reads it:
+// `grad` multiplies each counted token's dlogits row (1 / counted tokens for a mean, 1 for a
+// sum); the loss is the sum of the per-token losses divided by `denom` (counted tokens, or 1).
+struct Scale {
+  float grad;
+  float pad;
+  double denom;
+};
+
+// Which tokens count: a target equal to ignore_index (when ignore_on) contributes no loss and a
+// zero dlogits row; every other target counts (one outside [0, V) raises the data flag).
+struct Ignore {
+  int64_t index;
+  int on;
+  __host__ __device__ bool skip(int64_t t) const { return on && t == index; }
+};
+
+struct ScaleArgs {
+  const int64_t* t;     // all N targets
+  int64_t n;
+  Ignore ign;
+  int sum;              // 1: reduction "sum"
+  Scale* out;
+};
+
 struct LogitsArgs {
   const void* x;        // chunk's first token row, [rows][H]
   const void* W;        // [V][H]
@@ -34,6 +59,7 @@ struct CombineArgs {
   float* lse;           // [rows]
   float* loss_rows;     // [rows]
   int* flag;            // bit 0: a target outside [0, V)
+  Ignore ign;
   int pstride, tiles_n, rows, V;
 };
 
@@ -43,7 +69,8 @@ struct DlogitsArgs {
   const int64_t* t;
   int64_t ldz;
   int rows, V;
-  float inv_n;
+  Ignore ign;
+  const Scale* scale;
 };
 
 struct DxArgs {
@@ -57,6 +84,7 @@ struct DxArgs {
   int k_per_split, splits;
   int tiles_m, tiles_n;
   int dx_fp32;
+  int accumulate;       // 0: overwrite dx rows, 1: dx += G W (splits == 1 only; else in the reduce)
 };
 
 struct DxReduceArgs {
@@ -66,6 +94,7 @@ struct DxReduceArgs {
   int64_t count;        // rows * H
   int splits;
   int dx_fp32;
+  int accumulate;       // 0: overwrite, 1: add into dx
 };
 
 struct DwArgs {
@@ -83,6 +112,7 @@ struct FinalizeArgs {
   const float* loss_rows;
   float* loss;
   int64_t n;
+  const Scale* scale;   // loss = sum / scale->denom
 };
 
 // Fused variant, pass 2: per (token tile, vocabulary tile) the logits tile is recomputed,
@@ -96,7 +126,8 @@ struct FusedArgs {
   float* dw_acc;        // fp32 [V][H], zeroed before the first chunk
   int rows, H, V;
   int tiles_m, tiles_n, tiles_h;
-  float inv_n;
+  Ignore ign;
+  const Scale* scale;
 };
 
 struct FillArgs {
@@ -108,6 +139,7 @@ struct CastArgs {       // fp32 -> bf16, round to nearest even
   const float* src;
   void* dst;
   int64_t n;            // multiple of 4
+  int accumulate;       // 1: dst = bf16(dst + src)
 };
 
 hipError_t launch_logits(In in, const LogitsArgs& a, hipStream_t s);
@@ -120,5 +152,6 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_fused_bwd(const FusedArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(const FillArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t s);
+hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);
 
 }  // namespace flce

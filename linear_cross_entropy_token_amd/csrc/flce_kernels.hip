@@ -204,8 +204,12 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
     if (sm[p][rl] != ninf) SS += ss[p][rl] * fast_exp(sm[p][rl] - MM);
   const float lse = MM + fast_log(SS);
   const int64_t tv = a.t[r];
-  const bool ok = tv >= 0 && tv < a.V;
   a.lse[r] = lse;
+  if (a.ign.skip(tv)) {                 // ignored token: no loss
+    a.loss_rows[r] = 0.f;
+    return;
+  }
+  const bool ok = tv >= 0 && tv < a.V;
   a.loss_rows[r] = ok ? lse - a.zt[r] : __builtin_nanf("");
   if (!ok) atomicOr(a.flag, 1);
 }
@@ -219,12 +223,14 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
   const int64_t per_row = a.ldz / E;
   const int64_t total = per_row * a.rows;
   T* Z = static_cast<T*>(a.z);
+  const float scale = a.scale->grad;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(idx / per_row);
     const int c0 = (int)(idx - (int64_t)r * per_row) * E;
     const float l = a.lse[r];
     const int64_t tv = a.t[r];
+    const bool counted = !a.ign.skip(tv);   // an ignored token's row of G is zero
     u32x4* p = reinterpret_cast<u32x4*>(Z + (int64_t)r * a.ldz + c0);
     u32x4 v = *p;
     T* e = reinterpret_cast<T*>(&v);
@@ -232,10 +238,10 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
     for (int k = 0; k < E; ++k) {
       const int col = c0 + k;
       float g = 0.f;
-      if (col < a.V) {
+      if (counted && col < a.V) {
         g = fast_exp(to_f32<T>(e[k]) - l);
         if (col == tv) g -= 1.f;
-        g *= a.inv_n;
+        g *= scale;
       }
       e[k] = from_f32<T>(g);
     }
@@ -283,10 +289,19 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
         if (a.splits > 1) {
           *reinterpret_cast<f32x4*>(a.part + split * a.part_stride + o) = v;
         } else if (a.dx_fp32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + o) = v;
+          f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + o);
+          *p = a.accumulate ? *p + v : v;
         } else {
-          *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + o) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          u32x2* p = reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + o);
+          f32x4 w = v;
+          if (a.accumulate) {
+            const u32x2 old = *p;
+            w[0] += bf16_to_f32(old[0] & 0xffffu);
+            w[1] += bf16_to_f32(old[0] >> 16);
+            w[2] += bf16_to_f32(old[1] & 0xffffu);
+            w[3] += bf16_to_f32(old[1] >> 16);
+          }
+          *p = u32x2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
         }
       }
   }
@@ -298,10 +313,18 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
     f32x4 s = *reinterpret_cast<const f32x4*>(a.part + i);
     for (int k = 1; k < a.splits; ++k) s += *reinterpret_cast<const f32x4*>(a.part + k * a.part_stride + i);
     if (a.dx_fp32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + i) = s;
+      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.dx) + i);
+      *p = a.accumulate ? *p + s : s;
     } else {
-      *reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + i) =
-          u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+      u32x2* p = reinterpret_cast<u32x2*>(static_cast<bf16_t*>(a.dx) + i);
+      if (a.accumulate) {
+        const u32x2 old = *p;
+        s[0] += bf16_to_f32(old[0] & 0xffffu);
+        s[1] += bf16_to_f32(old[0] >> 16);
+        s[2] += bf16_to_f32(old[1] & 0xffffu);
+        s[3] += bf16_to_f32(old[1] >> 16);
+      }
+      *p = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
     }
   }
 }
@@ -413,7 +436,30 @@ __global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs a) {
     if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *a.loss = (float)(part[0] / (double)a.n);
+  if (threadIdx.x == 0) *a.loss = (float)(part[0] / a.scale->denom);
+}
+
+// ---------------------------------------------------------------------------
+// per-call normalisation: count the tokens whose target is not ignored (fixed order, one
+// block), then 1 / count (mean) or 1 (sum).  With no token counted a mean is 0 / 0 = NaN and
+// every dlogits row is zero, as for the mean cross-entropy of an all-ignored batch.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void scale_kernel(ScaleArgs a) {
+  __shared__ long long part[1024];
+  long long c = 0;
+  for (int64_t i = threadIdx.x; i < a.n; i += 1024) c += a.ign.skip(a.t[i]) ? 0 : 1;
+  part[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double denom = a.sum ? 1.0 : (double)part[0];
+    a.out->grad = (float)(1.0 / denom);
+    a.out->pad = 0.f;
+    a.out->denom = denom;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -468,6 +514,11 @@ hipError_t launch_dw(In in, const DwArgs& a, hipStream_t s) {
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(const ScaleArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(scale_kernel, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

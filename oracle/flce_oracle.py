@@ -23,8 +23,9 @@ Readings taken where the pages are silent or disagree:
   * reduction is the mean over all N tokens, and dx, dW carry the same 1/N:
     the code sample of the "core idea" section sums per chunk and divides
     loss, dx and dw by the global token count at the end;
-  * no bias, no ignore_index, no label smoothing (none is mentioned; the
-    projection in the code sample has no bias);
+  * no bias and no label smoothing (neither is mentioned; the projection in
+    the code sample has no bias); masked tokens (ignore_index) and the sum
+    reduction exist only in ``flce_ext``, which states its own readings;
   * W is [V,H] (the 128K-context guide at sigco.tistory.com prints an [H,V]
     weight in its chunked-CE snippet; the [V,H] layout of the FLCE page is
     taken).
@@ -38,7 +39,7 @@ from typing import Dict, Iterable
 import numpy as np
 
 __all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce",
-           "flce_rows", "logits_bytes"]
+           "flce_rows", "flce_ext", "logits_bytes"]
 
 
 def widen(arr: np.ndarray, dtype: str) -> np.ndarray:
@@ -113,6 +114,59 @@ def flce(x: np.ndarray, W: np.ndarray, t: np.ndarray) -> Dict[str, np.ndarray]:
     dx = G @ W
     dW = G.T @ x
     return {"loss": float(losses.mean()), "dx": dx, "dW": dW, "lse": lse, "losses": losses}
+
+
+def flce_ext(x: np.ndarray, W: np.ndarray, t: np.ndarray, reduction: str = "mean",
+             ignore_index=None) -> Dict[str, np.ndarray]:
+    """The same materialised computation with the loss options a training loop asks for.
+
+    The 128K-context training guide (sigco.tistory.com), strategy 1 (chunked
+    cross-entropy), computes the loss alone, summing per chunk and dividing
+    by the token count, through PyTorch's cross_entropy; its tips section
+    recommends gradient accumulation.  The pages define no masking, so the
+    conventions of that cross_entropy call are taken:
+
+      * a token whose target equals ``ignore_index`` counts for nothing: its
+        loss is 0 and its row of G is 0;
+      * ``reduction="mean"`` divides the summed loss and every counted row of
+        G by the number of counted tokens (0 counted tokens: the loss is
+        0 / 0 = NaN and G is all zero); ``"sum"`` divides by nothing.
+
+    With ``ignore_index=None`` and ``"mean"`` this is ``flce``.  Counted
+    targets must lie in [0, V).
+    """
+    if reduction not in ("mean", "sum"):
+        raise ValueError(reduction)
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    t = np.asarray(t, dtype=np.int64)
+    N = x.shape[0]
+    if N == 0:
+        raise ValueError("N must be positive")
+    counted = np.ones(N, dtype=bool) if ignore_index is None else (t != ignore_index)
+    tc = t[counted]
+    if tc.size and (tc.min() < 0 or tc.max() >= W.shape[0]):
+        raise ValueError("targets out of range")
+    n_counted = int(counted.sum())
+    Z = logits(x, W)
+    lse = row_logsumexp(Z)
+    losses = np.zeros(N)
+    rows = np.nonzero(counted)[0]
+    losses[rows] = lse[rows] - Z[rows, tc]
+    if reduction == "sum":
+        denom = 1.0
+        loss = float(losses.sum())
+    else:
+        denom = float(n_counted)
+        loss = float(losses.sum() / denom) if n_counted else float("nan")
+    G = np.zeros_like(Z)
+    if n_counted:
+        Gc = np.exp(Z[rows] - lse[rows, None])
+        Gc[np.arange(rows.size), tc] -= 1.0
+        G[rows] = Gc / denom
+    del Z
+    return {"loss": loss, "dx": G @ W, "dW": G.T @ x, "lse": lse, "losses": losses,
+            "counted": n_counted}
 
 
 def flce_rows(x: np.ndarray, W: np.ndarray, t: np.ndarray, rows: Iterable[int],

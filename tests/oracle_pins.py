@@ -194,3 +194,70 @@ def check_torch_autograd(flce, N=31, H=12, V=45, seed=6):
 ALL_CHECKS = [check_worked_examples, check_zero_weight, check_two_classes,
               check_finite_differences, check_invariants, check_shift_invariance,
               check_permutations, check_torch_autograd]
+
+
+# ---- pins of the loss options (flce_ext) -------------------------------------
+# Each check_ext_* takes an ``ext(x, W, t, reduction, ignore_index) -> dict``.
+
+def _ext_inputs(seed, N, H, V, ignore, frac=0.3):
+    rng = _rng(seed)
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.5
+    t = rng.integers(0, V, N)
+    if ignore is not None:
+        t[rng.random(N) < frac] = ignore
+    return x, W, t
+
+
+def check_ext_torch(ext, N=29, H=10, V=37, seed=7):
+    """Library routine: torch cross_entropy(reduction=..., ignore_index=...) with autograd,
+    fp64 on the CPU, including an in-range ignore_index and an all-ignored batch."""
+    import torch
+    import torch.nn.functional as F
+    cases = [(r, ign, 0.3) for r in ("mean", "sum") for ign in (None, -100, 5)]
+    cases += [("mean", -1, 1.0), ("sum", -1, 1.0)]
+    for k, (reduction, ign, frac) in enumerate(cases):
+        x, W, t = _ext_inputs(seed + k, N, H, V, ign, frac)
+        xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+        Wt = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+        loss = F.cross_entropy(xt @ Wt.T, torch.tensor(t), reduction=reduction,
+                               ignore_index=-100 if ign is None else ign)
+        loss.backward()
+        r = ext(x, W, t, reduction, ign)
+        what = f"torch {reduction} ignore={ign} frac={frac}"
+        if math.isnan(loss.item()):
+            assert math.isnan(r["loss"]), f"{what}: loss {r['loss']} (expected NaN)"
+        else:
+            _close(r["loss"], loss.item(), 1e-13, 1e-15, what + " loss")
+        _close(r["dx"], xt.grad.numpy(), 1e-11, 1e-15, what + " dx")
+        _close(r["dW"], Wt.grad.numpy(), 1e-11, 1e-15, what + " dW")
+
+
+def check_ext_drop_rows(ext, N=40, H=8, V=23, seed=8):
+    """Ignoring tokens is dropping them: against the plain definition (the pinned ``flce``)
+    on the kept rows, with zero gradient rows for the ignored ones; a sum is the mean times
+    the count."""
+    import oracle
+    x, W, t = _ext_inputs(seed, N, H, V, -7, 0.4)
+    kept = t != -7
+    ref = oracle.flce(x[kept], W, t[kept])
+    n = int(kept.sum())
+    for reduction, f in (("mean", 1.0), ("sum", float(n))):
+        r = ext(x, W, t, reduction, -7)
+        _close(r["loss"], ref["loss"] * f, 1e-12, 0, f"drop rows {reduction} loss")
+        _close(r["dx"][kept], ref["dx"] * f, 1e-11, 1e-15, f"drop rows {reduction} dx")
+        _close(r["dx"][~kept], np.zeros((N - n, H)), 0, 0, f"drop rows {reduction} ignored dx")
+        _close(r["dW"], ref["dW"] * f, 1e-11, 1e-15, f"drop rows {reduction} dW")
+
+
+def check_ext_defaults(ext, N=18, H=7, V=13, seed=9):
+    """No ignored token and the mean: the plain definition."""
+    import oracle
+    x, W, t = _ext_inputs(seed, N, H, V, None)
+    r, ref = ext(x, W, t, "mean", None), oracle.flce(x, W, t)
+    _close(r["loss"], ref["loss"], 1e-14, 0, "defaults loss")
+    _close(r["dx"], ref["dx"], 1e-13, 1e-16, "defaults dx")
+    _close(r["dW"], ref["dW"], 1e-13, 1e-16, "defaults dW")
+
+
+EXT_CHECKS = [check_ext_torch, check_ext_drop_rows, check_ext_defaults]

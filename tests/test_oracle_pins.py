@@ -83,6 +83,70 @@ def test_unmutated_copy_passes_all_pins():
         check(good)
 
 
+# ---- loss options (flce_ext) -------------------------------------------------
+
+def _ext(x, W, t, reduction, ignore_index):
+    return oracle.flce_ext(x, W, t, reduction=reduction, ignore_index=ignore_index)
+
+
+@pytest.mark.parametrize("check", pins.EXT_CHECKS, ids=lambda c: c.__name__)
+def test_ext_pin(check):
+    check(_ext)
+
+
+def _ext_mutant(kind):
+    def ext(x, W, t, reduction, ignore_index):
+        x = np.asarray(x, dtype=np.float64)
+        W = np.asarray(W, dtype=np.float64)
+        t = np.asarray(t, dtype=np.int64)
+        N = x.shape[0]
+        counted = np.ones(N, bool) if ignore_index is None else t != ignore_index
+        tt = np.where(counted, t, 0)
+        Z = x @ W.T
+        lse = fo.row_logsumexp(Z)
+        losses = lse - Z[np.arange(N), tt]
+        if kind != "ignored_rows_keep_loss":
+            losses = np.where(counted, losses, 0.0)
+        n = int(counted.sum())
+        denom = float(N) if kind == "mean_over_all_tokens" else float(n)
+        if reduction == "sum" and kind != "sum_divides":
+            denom = 1.0
+        if n == 0 and reduction == "mean":
+            loss = 0.0 if kind == "all_ignored_zero_loss" else float("nan")
+        else:
+            loss = float(losses.sum() / denom)
+        G = np.exp(Z - lse[:, None])
+        G[np.arange(N), tt] -= 1.0
+        if kind != "ignored_rows_keep_grad":
+            G[~counted] = 0.0
+        G /= max(denom, 1.0) if n == 0 else denom
+        return {"loss": loss, "dx": G @ W, "dW": G.T @ x}
+    return ext
+
+
+EXT_MUTANTS = ["mean_over_all_tokens", "ignored_rows_keep_grad", "ignored_rows_keep_loss",
+               "sum_divides", "all_ignored_zero_loss"]
+
+
+@pytest.mark.parametrize("kind", EXT_MUTANTS)
+def test_ext_pins_catch_planted_mistake(kind):
+    bad = _ext_mutant(kind)
+    caught = []
+    with np.errstate(all="ignore"):
+        for check in pins.EXT_CHECKS:
+            try:
+                check(bad)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {kind!r}"
+
+
+def test_ext_unmutated_copy_passes():
+    good = _ext_mutant("none")
+    for check in pins.EXT_CHECKS:
+        check(good)
+
+
 # ---- other properties of the oracle ---------------------------------------
 
 def test_rows_match_full():
