@@ -27,7 +27,8 @@ static_assert(kTile == kTileM && kTile == kTileN, "tile sizes of the dispatcher 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
   constexpr int kEpiBytes = 2 * kWaveCols * kTile * (int)sizeof(float) + kTile * (int)sizeof(int);
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes + kEpiBytes];
+  static_assert(kSmemBytes + kEpiBytes <= kDeepRingBytes, "epilogue scratch fits behind the z tile");
+  __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const int tid = threadIdx.x;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
   int tm, tn;
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
     rel = (d >= 0 && d < kTile) ? (int)d : -1;
   }
   f32x16 acc[kColBlocks][4];
-  gemm_tile<T>(acc, smem, C, R, 0, a.H);
+  gemm_tile_deep_c<T>(acc, smem, C, R, 0, a.H);
 
   const Frag f = frag_coords();
   // [2][kWaveCols][kTile]: per column-wave max, then sum; then the target column per row.  The
