@@ -39,6 +39,11 @@ SMALL = [
     ("bf16_N1", 1, 64, 1001, "bf16", 0, None),
     ("bf16_H64_V1001", 300, 64, 1001, "bf16", 128, None),
     ("bf16_one_chunk", 512, 256, 3000, "bf16", 0, None),
+    # H = 264: a partial last k-slice in the logits GEMM and a partial second column tile in
+    # the dx and dW epilogues (dW read-modify-write over three chunks)
+    ("bf16_H264", 520, 264, 1300, "bf16", 200, None),
+    ("bf16_H264_fp32_grads", 520, 264, 1300, "bf16", 200, "fp32"),
+    ("fp32_H264", 200, 264, 900, "fp32", 64, None),
 ]
 
 
