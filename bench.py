@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -33,13 +34,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace runs (the part that decides the kernels)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(csrc: str = None) -> str:
+    """Fingerprint of the HIP sources' code (comments and layout excluded), used to tell whether
+    stored rocprofv3 traffic counters still describe the kernels."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "linear_cross_entropy_token_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "linear_cross_entropy_token_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

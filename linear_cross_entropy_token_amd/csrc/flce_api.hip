@@ -5,9 +5,10 @@
 // Linear Cross-Entropy" page (42jerrykim.github.io): for each chunk of C
 // tokens, project, turn the logits buffer into dlogits in place, produce dx
 // rows, accumulate dW; the loss and both gradients carry 1/N for the global
-// token count.  Unlike that page's listing, nothing synchronises the host
-// inside the loop: the per-token losses stay on the device and one final
-// kernel reduces them.
+// token count (with options: 1 / the count of tokens not ignored, or 1 for a
+// sum, counted on the device).  Unlike that page's listing, nothing
+// synchronises the host inside the loop: the per-token losses stay on the
+// device and one final kernel reduces them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

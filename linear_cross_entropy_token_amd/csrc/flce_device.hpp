@@ -8,12 +8,16 @@
 //    (fp32 inputs);
 //  * the contraction is walked in k-slices of 128 bytes per operand row
 //    (64 bf16 / 32 fp32, one full cache line per k-major row) through a
-//    2-stage LDS ring (2 x 64 KiB): operand tiles are copied HBM -> LDS by
-//    buffer_load ... lds (direct-to-LDS DMA, no VGPR staging), issued one
-//    slice ahead of the MFMAs that consume them; out-of-range rows/columns
-//    come back as zeros from the buffer range check, so ragged edges need no
-//    branches.  (Measured on MI355X: full-line requests with 2 stages beat
-//    half-line requests with 4 stages of 32 KiB on all three GEMMs.)
+//    2-stage LDS ring (2 x 64 KiB; the logits GEMM uses all 160 KiB, see
+//    gemm_tile_deep_c): operand tiles are copied HBM -> LDS by buffer_load
+//    ... lds (direct-to-LDS DMA, no VGPR staging), issued one slice ahead of
+//    the MFMAs that consume them; out-of-range rows/columns come back as
+//    zeros from the buffer range check, so ragged edges need no branches.
+//    (Measured on MI355X: full-line requests with 2 stages beat half-line
+//    requests with 4 stages of 32 KiB on all three GEMMs.)
+//  * the two waves of each SIMD run a ping-pong schedule (gemm_tile): one
+//    multiplies a whole k-slice from registers while the other reads the
+//    next fragments from LDS and issues copies;
 //  * an operand stored with the contraction index contiguous ("k-major": x
 //    and W for the logits, G for dx) is kept k-major in LDS and read with
 //    ds_read_b128; an operand whose contraction index is the ROW ("mn-major":

@@ -4,7 +4,8 @@
 // per-token log-sum-exp.  Pass 2 never writes a logits or dlogits tensor:
 // for each (256-token, 256-vocabulary) tile a workgroup
 //   1. recomputes z = x_tile W_tile^T on the MFMA engine (contraction over H),
-//   2. forms G = (exp(z - lse) - onehot(t)) / N and keeps it in LDS as a
+//   2. forms G = (exp(z - lse) - onehot(t)) * scale (1/N for the page's mean;
+//      zero rows for ignored tokens) and keeps it in LDS as a
 //      256 x 256 bf16 tile (the dlogits of the FLCE page's step 2, held
 //      on-chip as the "Unsloth deep architecture" page's streaming CE kernel
 //      does),

@@ -8,12 +8,15 @@
 //                chunk buffer (online-softmax statistics as on the "Unsloth
 //                deep architecture" page, streaming CE kernel).
 //   lse_combine  lse_n = M + ln sum_j s_j e^(m_j - M) over the vocab tiles,
-//                per-row loss lse_n - z[n, t_n].
-//   dlogits      G = (exp(z - lse) - onehot(t)) / N written over z
-//                (softmax - one_hot in the same buffer, step 2).
-//   dx           dx_c = G W (contraction over the vocabulary, split-K).
+//                per-row loss lse_n - z[n, t_n] (0 for an ignored token).
+//   dlogits      G = (exp(z - lse) - onehot(t)) * scale written over z
+//                (softmax - one_hot in the same buffer, step 2; scale = 1/N
+//                for the mean over N tokens, the page's reduction).
+//   dx           dx_c (+)= G W (contraction over the vocabulary, split-K).
 //   dw           dW (+)= G^T x_c (contraction over the chunk's tokens).
-// and once per call: finalize, loss = sum_n loss_n / N (deterministic).
+// and once per call: scale (count of the tokens that count, on the device)
+// before the chunks, finalize (loss = sum_n loss_n / count, deterministic)
+// after them.
 #include "flce_device.hpp"
 #include "flce_internal.hpp"
 
