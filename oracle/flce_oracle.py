@@ -39,7 +39,7 @@ from typing import Dict, Iterable
 import numpy as np
 
 __all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce",
-           "flce_rows", "flce_ext", "logits_bytes"]
+           "flce_rows", "flce_ext", "rmsnorm", "rmsnorm_backward", "rmsnorm_flce", "logits_bytes"]
 
 
 def widen(arr: np.ndarray, dtype: str) -> np.ndarray:
@@ -167,6 +167,49 @@ def flce_ext(x: np.ndarray, W: np.ndarray, t: np.ndarray, reduction: str = "mean
     del Z
     return {"loss": loss, "dx": G @ W, "dW": G.T @ x, "lse": lse, "losses": losses,
             "counted": n_counted}
+
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float):
+    """x = h / RMS(h) * gamma with RMS(h) = sqrt(mean_k h_k^2 + eps), per row; returns (x, rstd).
+
+    The RMSNorm definition of the "Unsloth deep architecture" page (section on RMSNorm and its
+    backward as one kernel); rstd = 1 / RMS(h) is the one value per row that page keeps for the
+    backward pass.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    rstd = 1.0 / np.sqrt((h * h).mean(axis=1) + float(eps))
+    return h * rstd[:, None] * np.asarray(gamma, dtype=np.float64)[None, :], rstd
+
+
+def rmsnorm_backward(dx: np.ndarray, h: np.ndarray, gamma: np.ndarray, rstd: np.ndarray):
+    """(dh, dgamma) for x = rmsnorm(h, gamma) given dL/dx.
+
+    dh_i = rstd (dx_i g_i - h_i rstd^2 / d * sum_k dx_k g_k h_k): the simplified input derivative
+    the same section gives (with 1 / RMS = rstd); dgamma_i = sum_n dx[n,i] h[n,i] rstd_n, the
+    derivative of x = h rstd gamma in gamma (the page names dgamma as the kernel's second output
+    but prints no formula for it).
+    """
+    dx = np.asarray(dx, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    d = h.shape[1]
+    s = (dx * g[None, :] * h).sum(axis=1)
+    dh = rstd[:, None] * (dx * g[None, :] - h * (rstd ** 2 * s / d)[:, None])
+    dgamma = (dx * h * rstd[:, None]).sum(axis=0)
+    return dh, dgamma
+
+
+def rmsnorm_flce(h: np.ndarray, gamma: np.ndarray, eps: float, W: np.ndarray, t: np.ndarray,
+                 reduction: str = "mean", ignore_index=None) -> Dict[str, np.ndarray]:
+    """The final RMSNorm in front of the LM head, then the loss: x = rmsnorm(h), loss of x W^T.
+
+    Returns loss, dh = dL/dh, dgamma = dL/dgamma, dW, lse and x (all fp64).
+    """
+    x, rstd = rmsnorm(h, gamma, eps)
+    r = flce_ext(x, W, t, reduction=reduction, ignore_index=ignore_index)
+    dh, dgamma = rmsnorm_backward(r["dx"], h, gamma, rstd)
+    return {"loss": r["loss"], "dh": dh, "dgamma": dgamma, "dW": r["dW"], "lse": r["lse"], "x": x,
+            "rstd": rstd, "dx": r["dx"]}
 
 
 def flce_rows(x: np.ndarray, W: np.ndarray, t: np.ndarray, rows: Iterable[int],

@@ -261,3 +261,85 @@ def check_ext_defaults(ext, N=18, H=7, V=13, seed=9):
 
 
 EXT_CHECKS = [check_ext_torch, check_ext_drop_rows, check_ext_defaults]
+
+
+# ---- pins of the RMSNorm in front of the head (rmsnorm_flce) ---------------
+# Each check_rms_* takes ``rf(h, gamma, eps, W, t, reduction, ignore_index) -> dict`` with
+# loss, dh, dgamma, dW.
+
+def _rms_inputs(seed, N, H, V):
+    rng = _rng(seed)
+    h = rng.standard_normal((N, H)) * 1.7
+    g = 1.0 + 0.3 * rng.standard_normal(H)
+    W = rng.standard_normal((V, H)) * 0.4
+    t = rng.integers(0, V, N)
+    return h, g, W, t
+
+
+def check_rms_torch(rf, N=23, H=12, V=19, seed=21):
+    """Library routines: torch rms_norm, then cross_entropy, with autograd, fp64 on the CPU
+    (a large eps so that a dropped eps shows)."""
+    import torch
+    import torch.nn.functional as F
+    for k, (reduction, ign, eps) in enumerate([("mean", None, 1e-2), ("sum", -100, 1e-6), ("mean", 3, 0.5)]):
+        h, g, W, t = _rms_inputs(seed + k, N, H, V)
+        if ign is not None:
+            t[_rng(seed + 50 + k).random(N) < 0.3] = ign
+        ht = torch.tensor(h, requires_grad=True)
+        gt = torch.tensor(g, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        x = F.rms_norm(ht, (H,), gt, eps)
+        loss = F.cross_entropy(x @ Wt.T, torch.tensor(t), reduction=reduction,
+                               ignore_index=-100 if ign is None else ign)
+        loss.backward()
+        r = rf(h, g, eps, W, t, reduction, ign)
+        what = f"rms torch {reduction} ignore={ign} eps={eps}"
+        _close(r["loss"], loss.item(), 1e-12, 1e-15, what + " loss")
+        _close(r["dh"], ht.grad.numpy(), 1e-10, 1e-14, what + " dh")
+        _close(r["dgamma"], gt.grad.numpy(), 1e-10, 1e-14, what + " dgamma")
+        _close(r["dW"], Wt.grad.numpy(), 1e-10, 1e-14, what + " dW")
+
+
+def check_rms_finite_differences(rf, N=3, H=5, V=4, seed=22, eps=1e-6):
+    """Central differences of the loss in h and gamma (fp64)."""
+    h, g, W, t = _rms_inputs(seed, N, H, V)
+    r = rf(h, g, 1e-3, W, t, "mean", None)
+    num_h = np.zeros_like(h)
+    for i in range(N):
+        for j in range(H):
+            hp, hm = h.copy(), h.copy()
+            hp[i, j] += eps
+            hm[i, j] -= eps
+            num_h[i, j] = (rf(hp, g, 1e-3, W, t, "mean", None)["loss"]
+                           - rf(hm, g, 1e-3, W, t, "mean", None)["loss"]) / (2 * eps)
+    num_g = np.zeros_like(g)
+    for j in range(H):
+        gp, gm = g.copy(), g.copy()
+        gp[j] += eps
+        gm[j] -= eps
+        num_g[j] = (rf(h, gp, 1e-3, W, t, "mean", None)["loss"] - rf(h, gm, 1e-3, W, t, "mean", None)["loss"]) / (2 * eps)
+    _close(r["dh"], num_h, 1e-6, 1e-9, "rms finite differences dh")
+    _close(r["dgamma"], num_g, 1e-6, 1e-9, "rms finite differences dgamma")
+
+
+def check_rms_scale_invariance(rf, N=17, H=9, V=11, seed=23, c=7.5):
+    """With eps = 0, scaling h by c > 0 leaves x, the loss, dW and dgamma unchanged and divides dh by c."""
+    h, g, W, t = _rms_inputs(seed, N, H, V)
+    a = rf(h, g, 0.0, W, t, "mean", None)
+    b = rf(c * h, g, 0.0, W, t, "mean", None)
+    _close(b["loss"], a["loss"], 1e-13, 0, "rms scale loss")
+    _close(b["dW"], a["dW"], 1e-11, 1e-15, "rms scale dW")
+    _close(b["dgamma"], a["dgamma"], 1e-11, 1e-15, "rms scale dgamma")
+    _close(b["dh"] * c, a["dh"], 1e-11, 1e-15, "rms scale dh")
+
+
+def check_rms_zero_gamma(rf, N=13, H=6, V=10, seed=24):
+    """gamma = 0: x = 0, so the loss is ln V exactly, dW = 0 and dh = 0."""
+    h, g, W, t = _rms_inputs(seed, N, H, V)
+    r = rf(h, np.zeros_like(g), 1e-5, W, t, "mean", None)
+    _close(r["loss"], math.log(V), 1e-14, 0, "rms zero gamma loss")
+    _close(r["dW"], np.zeros_like(W), 0, 1e-17, "rms zero gamma dW")
+    _close(r["dh"], np.zeros_like(h), 0, 1e-17, "rms zero gamma dh")
+
+
+RMS_CHECKS = [check_rms_torch, check_rms_finite_differences, check_rms_scale_invariance, check_rms_zero_gamma]

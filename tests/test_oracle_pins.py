@@ -147,6 +147,58 @@ def test_ext_unmutated_copy_passes():
         check(good)
 
 
+# ---- RMSNorm in front of the head (rmsnorm_flce) ---------------------------
+
+def _rf(h, g, eps, W, t, reduction, ignore_index):
+    return oracle.rmsnorm_flce(h, g, eps, W, t, reduction=reduction, ignore_index=ignore_index)
+
+
+@pytest.mark.parametrize("check", pins.RMS_CHECKS, ids=lambda c: c.__name__)
+def test_rms_pin(check):
+    check(_rf)
+
+
+def _rms_mutant(kind):
+    def rf(h, g, eps, W, t, reduction, ignore_index):
+        h = np.asarray(h, dtype=np.float64)
+        g = np.asarray(g, dtype=np.float64)
+        d = h.shape[1]
+        ms = (h * h).mean(axis=1) + (0.0 if kind == "no_eps" else eps)
+        rstd = 1.0 / (ms if kind == "rms_no_sqrt" else np.sqrt(ms))
+        x = h * rstd[:, None] * g[None, :]
+        r = oracle.flce_ext(x, W, t, reduction=reduction, ignore_index=ignore_index)
+        dx = r["dx"]
+        s = (dx * g[None, :] * h).sum(axis=1)
+        dd = 1.0 if kind == "dh_missing_1_over_d" else float(d)
+        sign = 1.0 if kind == "dh_plus" else -1.0
+        dh = rstd[:, None] * (dx * g[None, :] + sign * h * (rstd ** 2 * s / dd)[:, None])
+        dgamma = (dx * h * (1.0 if kind == "dgamma_no_rstd" else rstd[:, None])).sum(axis=0)
+        return {"loss": r["loss"], "dh": dh, "dgamma": dgamma, "dW": r["dW"]}
+    return rf
+
+
+RMS_MUTANTS = ["no_eps", "rms_no_sqrt", "dh_missing_1_over_d", "dh_plus", "dgamma_no_rstd"]
+
+
+@pytest.mark.parametrize("kind", RMS_MUTANTS)
+def test_rms_pins_catch_planted_mistake(kind):
+    bad = _rms_mutant(kind)
+    caught = []
+    with np.errstate(all="ignore"):
+        for check in pins.RMS_CHECKS:
+            try:
+                check(bad)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {kind!r}"
+
+
+def test_rms_unmutated_copy_passes():
+    good = _rms_mutant("none")
+    for check in pins.RMS_CHECKS:
+        check(good)
+
+
 # ---- other properties of the oracle ---------------------------------------
 
 def test_rows_match_full():
