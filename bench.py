@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--ignore-frac", type=float, default=0.0,
                     help="set this fraction of the targets (seeded) to -100 and pass ignore_index=-100")
     ap.add_argument("--accumulate", action="store_true", help="add the gradients into dx and dW")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="RMSNorm in front of the head (flce_rmsnorm_forward_backward): the workload's x "
+                         "becomes the hidden states, gamma ~ 1 + 0.2 N(0,1) (seeded), eps 1e-6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--materialised", action="store_true",
                     help="also measure the peak HBM of the materialised-logits PyTorch path")
@@ -205,6 +208,10 @@ def main():
     ignore = -100 if args.ignore_frac > 0 else None
     if args.forward_only and args.accumulate:
         raise SystemExit("--forward-only and --accumulate exclude each other")
+    gamma = None
+    if args.rmsnorm:
+        g32 = (1.0 + 0.2 * np.random.default_rng(w.seed + 104729).standard_normal(w.H)).astype(np.float32)
+        gamma = torch.from_numpy(g32).to(dev).to(x.dtype)
     log(f"[bench] inputs on device in {time.perf_counter() - t0:.1f} s")
 
     torch.cuda.synchronize()
@@ -215,12 +222,18 @@ def main():
     loss = torch.empty((), dtype=torch.float32, device=dev)
     dx = torch.empty(x.shape, dtype=gdt, device=dev)
     dW = torch.empty(W.shape, dtype=gdt, device=dev)
+    dgamma = torch.empty((w.H,), dtype=gdt, device=dev) if args.rmsnorm else None
     base_alloc = torch.cuda.memory_allocated()
     free0, _ = torch.cuda.mem_get_info()
-    if not args.forward_only:   # a forward-only call sizes its (smaller) workspace itself
+    if not args.forward_only and not args.rmsnorm:   # the other calls size their workspace themselves
         f.reserve(w.N, w.H, w.V, chunk)
     free1, total_mem = torch.cuda.mem_get_info()
-    ws_bytes = f.workspace_bytes(w.N, w.H, w.V, chunk, forward_only=args.forward_only)
+    if args.rmsnorm:
+        ws_bytes = flce.flce_rmsnorm_workspace_bytes(
+            f.handle, w.N, w.H, w.V, chunk,
+            flce._options(args.reduction, None, flce.FLCE_FORWARD_ONLY if args.forward_only else 0))
+    else:
+        ws_bytes = f.workspace_bytes(w.N, w.H, w.V, chunk, forward_only=args.forward_only)
     eff_chunk = flce.flce_effective_chunk(w.N, w.H, w.V, chunk)
 
     out = (loss, dx, dW, None)
@@ -230,6 +243,13 @@ def main():
         dW.zero_()
 
     def step():
+        if args.rmsnorm:
+            if args.forward_only:
+                return f.rmsnorm_forward(x, gamma, W, t, eps=1e-6, chunk=chunk, reduction=args.reduction,
+                                         ignore_index=ignore)
+            return f.rmsnorm_forward_backward(x, gamma, W, t, eps=1e-6, chunk=chunk,
+                                              out=(loss, dx, dgamma, dW, None), reduction=args.reduction,
+                                              ignore_index=ignore, accumulate=args.accumulate)
         if args.forward_only:
             return f.forward(x, W, t, chunk=chunk, reduction=args.reduction, ignore_index=ignore)
         return f.forward_backward(x, W, t, chunk=chunk, out=out, reduction=args.reduction, ignore_index=ignore,
@@ -323,7 +343,7 @@ def main():
                    "grad_dtype": "fp32" if args.grad_dtype == "fp32" else w.dtype,
                    "mode": "forward" if args.forward_only else "forward+backward",
                    "reduction": args.reduction, "ignore_frac": args.ignore_frac,
-                   "accumulate": args.accumulate, "parallelism": "single GPU"},
+                   "accumulate": args.accumulate, "rmsnorm": args.rmsnorm, "parallelism": "single GPU"},
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
     }

@@ -145,6 +145,30 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
 size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
                                 const flce_options_t* opt);
 
+/* The final RMSNorm of the model in front of the head, then the loss (an upstream
+ * fusion).  From the "Unsloth deep architecture" page, section on RMSNorm and its backward as
+ * one kernel:
+ *   x = hidden / RMS(hidden) * gamma,  RMS(h) = sqrt(mean_k h_k^2 + eps)  (per token row),
+ * then the loss of flce_forward_backward_opt on x.  Returns dhidden = d loss / d hidden,
+ * dgamma = d loss / d gamma (sum over tokens of dx * hidden / RMS) and dW.  Processed per token
+ * chunk: the chunk's x (input dtype, rounded once) and its fp32 d loss / d x live only in the
+ * workspace; neither reaches HBM for all N.
+ *   hidden  [N,H]  cfg.in_dtype, read-only         gamma   [H]  cfg.in_dtype, read-only
+ *   dhidden [N,H]  cfg.dx_dtype                    dgamma  [H]  cfg.dw_dtype
+ *   dW      [V,H]  cfg.dw_dtype                    eps >= 0 (finite)
+ * Options as for flce_forward_backward_opt (accumulate adds into dhidden, dgamma and dW;
+ * forward only needs none of them).  Chunked variant only; H <= 32768.
+ * Errors: INVALID_ARG (NULL pointers, bad options, eps < 0 or NaN, aliasing outputs),
+ * UNSUPPORTED (fused variant, H > 32768, alignment, size limits), OOM, HIP. */
+flce_status_t flce_rmsnorm_forward_backward(flce_handle_t h, const void* hidden, const void* gamma, float eps,
+                                            const void* W, const int64_t* targets, int64_t N, int64_t H,
+                                            int64_t V, int64_t chunk, const flce_options_t* opt, float* loss,
+                                            void* dhidden, void* dgamma, void* dW, float* lse, void* stream);
+
+/* Workspace bytes flce_rmsnorm_forward_backward needs for these sizes and options (0 if invalid). */
+size_t flce_rmsnorm_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    const flce_options_t* opt);
+
 /* Token chunk the call would use (for bf16 inputs): chunk clamped to [1, N] when positive; for
  * chunk <= 0 the size rule of the FLCE page's trade-offs section, next_pow2(ceil(N / ceil(V/H))),
  * raised to at least 4096 tokens (on MI355X the chunk's GEMMs run faster with the longer token

@@ -20,6 +20,7 @@ __all__ = [
     "library_path", "load_library", "flce_create", "flce_destroy", "flce_forward_backward",
     "flce_forward_backward_ex", "flce_forward_backward_opt", "Options", "FLCE_MEAN", "FLCE_SUM",
     "FLCE_ACCUMULATE", "FLCE_FORWARD_ONLY", "flce_effective_chunk", "flce_workspace_bytes", "flce_workspace_bytes_opt", "flce_reserve",
+    "flce_rmsnorm_forward_backward", "flce_rmsnorm_workspace_bytes",
     "flce_check", "flce_status_string", "flce_profile_enable", "flce_profile_read", "KernelStat",
     "FusedLinearCrossEntropy",
 ]
@@ -89,6 +90,11 @@ def load_library() -> ctypes.CDLL:
     lib.flce_workspace_bytes.restype = ctypes.c_size_t
     lib.flce_workspace_bytes_opt.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(Options)]
     lib.flce_workspace_bytes_opt.restype = ctypes.c_size_t
+    lib.flce_rmsnorm_forward_backward.argtypes = [vp, vp, vp, ctypes.c_float, vp, vp, i64, i64, i64, i64,
+                                                  ctypes.POINTER(Options), vp, vp, vp, vp, vp, vp]
+    lib.flce_rmsnorm_forward_backward.restype = i32
+    lib.flce_rmsnorm_workspace_bytes.argtypes = [vp, i64, i64, i64, i64, ctypes.POINTER(Options)]
+    lib.flce_rmsnorm_workspace_bytes.restype = ctypes.c_size_t
     lib.flce_reserve.argtypes = [vp, i64, i64, i64, i64]
     lib.flce_reserve.restype = i32
     lib.flce_check.argtypes = [vp, vp]
@@ -148,6 +154,18 @@ def flce_workspace_bytes(handle, N, H, V, chunk) -> int:
 def flce_workspace_bytes_opt(handle, N, H, V, chunk, opt) -> int:
     return load_library().flce_workspace_bytes_opt(handle, N, H, V, chunk,
                                                    ctypes.byref(opt) if opt is not None else None)
+
+
+def flce_rmsnorm_forward_backward(handle, hidden, gamma, eps, W, targets, N, H, V, chunk, opt, loss, dhidden,
+                                  dgamma, dW, lse, stream) -> int:
+    return load_library().flce_rmsnorm_forward_backward(handle, hidden, gamma, float(eps), W, targets, N, H, V,
+                                                        chunk, ctypes.byref(opt) if opt is not None else None,
+                                                        loss, dhidden, dgamma, dW, lse, stream)
+
+
+def flce_rmsnorm_workspace_bytes(handle, N, H, V, chunk, opt) -> int:
+    return load_library().flce_rmsnorm_workspace_bytes(handle, N, H, V, chunk,
+                                                       ctypes.byref(opt) if opt is not None else None)
 
 
 def flce_reserve(handle, N, H, V, chunk) -> int:
@@ -296,6 +314,61 @@ class FusedLinearCrossEntropy:
         if st != 0:
             raise FlceError(st, "flce_forward_backward_opt")
         return (loss, lse) if with_lse else loss
+
+
+def _rmsnorm_call(self, hidden, gamma, W, t, eps, chunk, with_lse, out, stream, reduction, ignore_index,
+                  flags):
+    import torch
+    N, H = hidden.shape
+    V = W.shape[0]
+    grads = not (flags & FLCE_FORWARD_ONLY)
+    if out is None:
+        if flags & FLCE_ACCUMULATE:
+            raise ValueError("accumulate needs the dhidden, dgamma and dW to add into (out=...)")
+        loss = torch.empty((), dtype=torch.float32, device=hidden.device)
+        dh = torch.empty((N, H), dtype=self.dx_dtype, device=hidden.device) if grads else None
+        dg = torch.empty((H,), dtype=self.dw_dtype, device=hidden.device) if grads else None
+        dW = torch.empty((V, H), dtype=self.dw_dtype, device=hidden.device) if grads else None
+        lse = torch.empty((N,), dtype=torch.float32, device=hidden.device) if with_lse else None
+    else:
+        loss, dh, dg, dW, lse = out
+    for name, ten in (("hidden", hidden), ("gamma", gamma), ("W", W), ("targets", t), ("dhidden", dh),
+                      ("dgamma", dg), ("dW", dW)):
+        if ten is not None and not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if hidden.dtype != self.in_dtype or gamma.dtype != self.in_dtype or W.dtype != self.in_dtype \
+            or t.dtype != torch.int64:
+        raise ValueError("dtype mismatch with the handle's configuration")
+    s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
+    ptr = (lambda ten: ten.data_ptr() if ten is not None else None)
+    st = flce_rmsnorm_forward_backward(self.handle, hidden.data_ptr(), gamma.data_ptr(), eps, W.data_ptr(),
+                                       t.data_ptr(), N, H, V, chunk, _options(reduction, ignore_index, flags),
+                                       loss.data_ptr(), ptr(dh), ptr(dg), ptr(dW), ptr(lse), s.cuda_stream)
+    if st != 0:
+        raise FlceError(st, "flce_rmsnorm_forward_backward")
+    return loss, dh, dg, dW, lse
+
+
+def _rmsnorm_forward_backward(self, hidden, gamma, W, t, eps: float = 1e-6, chunk: int = 0, with_lse: bool = False,
+                              out=None, stream=None, reduction: str = "mean", ignore_index: Optional[int] = None,
+                              accumulate: bool = False):
+    """RMSNorm (x = hidden / RMS(hidden) * gamma) in front of the head, then the loss; returns
+    ``(loss, dhidden, dgamma, dW)`` (and ``lse`` if asked).  ``out`` = (loss, dhidden, dgamma, dW, lse)."""
+    loss, dh, dg, dW, lse = _rmsnorm_call(self, hidden, gamma, W, t, eps, chunk, with_lse, out, stream, reduction,
+                                          ignore_index, FLCE_ACCUMULATE if accumulate else 0)
+    return (loss, dh, dg, dW, lse) if with_lse else (loss, dh, dg, dW)
+
+
+def _rmsnorm_forward(self, hidden, gamma, W, t, eps: float = 1e-6, chunk: int = 0, with_lse: bool = False,
+                     stream=None, reduction: str = "mean", ignore_index: Optional[int] = None):
+    """Loss only (and lse if asked) of RMSNorm + head."""
+    loss, _, _, _, lse = _rmsnorm_call(self, hidden, gamma, W, t, eps, chunk, with_lse, None, stream, reduction,
+                                       ignore_index, FLCE_FORWARD_ONLY)
+    return (loss, lse) if with_lse else loss
+
+
+FusedLinearCrossEntropy.rmsnorm_forward_backward = _rmsnorm_forward_backward
+FusedLinearCrossEntropy.rmsnorm_forward = _rmsnorm_forward
 
 
 def _options(reduction: str, ignore_index: Optional[int], flags: int) -> Options:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflce.so")
-SOURCES = ["flce_kernels.hip", "flce_fused.hip", "flce_api.hip"]
+SOURCES = ["flce_kernels.hip", "flce_fused.hip", "flce_rmsnorm.hip", "flce_api.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

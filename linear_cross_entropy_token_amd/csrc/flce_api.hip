@@ -39,6 +39,7 @@ struct Plan {
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
   size_t off_scale = 0;                  // flce::Scale of the call
+  size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
   bool fused = false;
   bool grads = true;                     // false: forward only (no logits buffer, no accumulators)
   size_t total = 0;
@@ -58,11 +59,11 @@ namespace {
 
 enum Kernel {
   K_LOGITS = 0, K_COMBINE, K_DLOGITS, K_DX, K_DX_REDUCE, K_DW, K_FINALIZE, K_FUSED_BWD, K_FILL, K_CAST,
-  K_SCALE, K_COUNT
+  K_SCALE, K_RMS_FWD, K_RMS_BWD, K_RMS_REDUCE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"logits_lse", "lse_combine", "dlogits", "dx", "dx_reduce",
                                            "dw", "finalize", "fused_bwd", "fill_zero", "cast_bf16",
-                                           "scale"};
+                                           "scale", "rms_fwd", "rms_bwd", "rms_reduce"};
 
 struct Mark {
   int kind;                 // Kernel, or -1 for the event that closes a call
@@ -180,7 +181,8 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
-Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true) {
+Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true,
+               bool rms = false) {
   Plan p;
   p.N = N;
   p.H = H;
@@ -217,6 +219,15 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (p.fused && grads && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
   p.off_dwacc = off;
   if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
+  if (rms) {   // the chunk's normalised rows, their fp32 dL/dx, rstd, dgamma partials and sum
+    p.off_xc = off;    off = align_up(off + (size_t)p.C * H * in_size(cfg));
+    p.off_dxc = off;   if (grads) off = align_up(off + (size_t)p.C * H * sizeof(float));
+    p.off_rstd = off;  off = align_up(off + (size_t)p.C * sizeof(float));
+    p.off_rpart = off;
+    if (grads) off = align_up(off + (size_t)cdiv(p.C, flce::kRmsRowsPerBlock) * H * sizeof(float));
+    p.off_dgacc = off;
+    if (grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)H * sizeof(float));
+  }
   p.total = off;
   return p;
 }
@@ -284,9 +295,17 @@ flce_status_t launch_scale(flce_handle_s* h, const Plan& p, const Opts& o, const
   return FLCE_OK;
 }
 
-flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
-                          const int64_t* t, float* loss, void* dx, void* dW, float* lse_out,
-                          hipStream_t st) {
+// Where one chunk's dx rows go.
+struct DxOut {
+  void* p;          // chunk's first row
+  bool fp32;
+  bool accumulate;
+};
+
+// One chunk of the token-chunked path: logits + statistics, combine, and (with gradients)
+// dlogits, dx rows of the chunk, dW update.  x_c: the chunk's first row of x.
+flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t s, int rows, const void* x_c,
+                         const void* W, const int64_t* t, float* lse, const DxOut& dxo, void* dW, hipStream_t st) {
   const flce_config_t& cfg = h->cfg;
   const In in = cfg.in_dtype == FLCE_BF16 ? In::BF16 : In::FP32;
   const size_t es = in_size(cfg);
@@ -295,125 +314,197 @@ flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const Opts& o, const 
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
   float* ps = reinterpret_cast<float*>(ws + p.off_ps);
   float* zt = reinterpret_cast<float*>(ws + p.off_zt);
-  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   float* part = reinterpret_cast<float*>(ws + p.off_part);
-  const size_t dx_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
   const flce::Scale* scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
-  const double b_in = (double)es, b_dx = (double)dx_es;
+  const double b_in = (double)es, b_dx = dxo.fp32 ? 4.0 : 2.0;
   const double b_dw = cfg.dw_dtype == FLCE_BF16 ? 2.0 : 4.0;
   const double VH = (double)p.V * (double)p.H;
-  const flce_status_t sc = launch_scale(h, p, o, t, st);
-  if (sc != FLCE_OK) return sc;
+  const int tiles_m = (int)cdiv(rows, kTile);
+  const double gemm_flops = 2.0 * rows * VH;
+  const double zbytes = o.grads ? (double)rows * (double)p.V * b_in : 0.0;
 
-  for (int64_t s = 0; s < p.N; s += p.C) {
-    const int rows = (int)std::min(p.C, p.N - s);
-    const int tiles_m = (int)cdiv(rows, kTile);
-    const double gemm_flops = 2.0 * rows * VH;
-    const double zbytes = o.grads ? (double)rows * (double)p.V * b_in : 0.0;
+  flce::LogitsArgs la{};
+  la.x = x_c;
+  la.W = W;
+  la.t = t + s;
+  la.z = o.grads ? z : nullptr;   // forward only: statistics, no logits buffer
+  la.pm = pm;
+  la.ps = ps;
+  la.zt = zt + s;
+  la.ldz = p.Vp;
+  la.pstride = (int)p.C;
+  la.rows = rows;
+  la.H = (int)p.H;
+  la.V = (int)p.V;
+  la.tiles_m = tiles_m;
+  la.tiles_n = p.tiles_v;
+  FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
+  FLCE_LAUNCH(flce::launch_logits(in, la, st));
 
-    flce::LogitsArgs la{};
-    la.x = static_cast<const char*>(x) + (size_t)s * p.H * es;
-    la.W = W;
-    la.t = t + s;
-    la.z = o.grads ? z : nullptr;   // forward only: statistics, no logits buffer
-    la.pm = pm;
-    la.ps = ps;
-    la.zt = zt + s;
-    la.ldz = p.Vp;
-    la.pstride = (int)p.C;
-    la.rows = rows;
-    la.H = (int)p.H;
-    la.V = (int)p.V;
-    la.tiles_m = tiles_m;
-    la.tiles_n = p.tiles_v;
-    FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
-    FLCE_LAUNCH(flce::launch_logits(in, la, st));
+  flce::CombineArgs ca{};
+  ca.pm = pm;
+  ca.ps = ps;
+  ca.zt = zt + s;
+  ca.t = t + s;
+  ca.lse = lse + s;
+  ca.loss_rows = loss_rows + s;
+  ca.flag = h->flag;
+  ca.ign = o.ign;
+  ca.pstride = (int)p.C;
+  ca.tiles_n = p.tiles_v;
+  ca.rows = rows;
+  ca.V = (int)p.V;
+  FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
+  FLCE_LAUNCH(flce::launch_combine(ca, st));
+  if (!o.grads) return FLCE_OK;
 
-    flce::CombineArgs ca{};
-    ca.pm = pm;
-    ca.ps = ps;
-    ca.zt = zt + s;
-    ca.t = t + s;
-    ca.lse = lse + s;
-    ca.loss_rows = loss_rows + s;
-    ca.flag = h->flag;
-    ca.ign = o.ign;
-    ca.pstride = (int)p.C;
-    ca.tiles_n = p.tiles_v;
-    ca.rows = rows;
-    ca.V = (int)p.V;
-    FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
-    FLCE_LAUNCH(flce::launch_combine(ca, st));
-    if (!o.grads) continue;
+  flce::DlogitsArgs ga{};
+  ga.z = z;
+  ga.lse = lse + s;
+  ga.t = t + s;
+  ga.ldz = p.Vp;
+  ga.rows = rows;
+  ga.V = (int)p.V;
+  ga.ign = o.ign;
+  ga.scale = scale;
+  FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes, st));
+  FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
 
-    flce::DlogitsArgs ga{};
-    ga.z = z;
-    ga.lse = lse + s;
-    ga.t = t + s;
-    ga.ldz = p.Vp;
-    ga.rows = rows;
-    ga.V = (int)p.V;
-    ga.ign = o.ign;
-    ga.scale = scale;
-    FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes, st));
-    FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
-
-    flce::DxArgs xa{};
-    xa.g = z;
-    xa.W = W;
-    xa.part = part;
-    xa.dx = static_cast<char*>(dx) + (size_t)s * p.H * dx_es;
-    xa.ldg = p.Vp;
-    xa.part_stride = p.C * p.H;
-    xa.rows = rows;
-    xa.H = (int)p.H;
-    xa.V = (int)p.V;
-    xa.k_per_split = (int)p.k_per_split;
-    xa.splits = p.splits;
-    xa.tiles_m = tiles_m;
-    xa.tiles_n = p.tiles_h;
-    xa.dx_fp32 = cfg.dx_dtype == FLCE_FP32;
-    xa.accumulate = o.accumulate;
-    FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
-    FLCE_LAUNCH(flce::launch_dx(in, xa, st));
-    if (p.splits > 1) {
-      flce::DxReduceArgs ra{};
-      ra.part = part;
-      ra.dx = xa.dx;
-      ra.part_stride = xa.part_stride;
-      ra.count = (int64_t)rows * p.H;
-      ra.splits = p.splits;
-      ra.dx_fp32 = xa.dx_fp32;
-      ra.accumulate = o.accumulate;
-      FLCE_LAUNCH(mark(h, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
-      FLCE_LAUNCH(flce::launch_dx_reduce(ra, st));
-    }
-
-    flce::DwArgs wa{};
-    wa.g = z;
-    wa.x = la.x;
-    wa.dW = dW;
-    wa.ldg = p.Vp;
-    wa.rows = rows;
-    wa.H = (int)p.H;
-    wa.V = (int)p.V;
-    wa.tiles_m = p.tiles_v;
-    wa.tiles_n = p.tiles_h;
-    wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
-    wa.accumulate = s > 0 || o.accumulate;
-    FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
-                     zbytes + (double)rows * p.H * b_in + VH * b_dw * (wa.accumulate ? 2.0 : 1.0), st));
-    FLCE_LAUNCH(flce::launch_dw(in, wa, st));
+  flce::DxArgs xa{};
+  xa.g = z;
+  xa.W = W;
+  xa.part = part;
+  xa.dx = dxo.p;
+  xa.ldg = p.Vp;
+  xa.part_stride = p.C * p.H;
+  xa.rows = rows;
+  xa.H = (int)p.H;
+  xa.V = (int)p.V;
+  xa.k_per_split = (int)p.k_per_split;
+  xa.splits = p.splits;
+  xa.tiles_m = tiles_m;
+  xa.tiles_n = p.tiles_h;
+  xa.dx_fp32 = dxo.fp32;
+  xa.accumulate = dxo.accumulate;
+  FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
+  FLCE_LAUNCH(flce::launch_dx(in, xa, st));
+  if (p.splits > 1) {
+    flce::DxReduceArgs ra{};
+    ra.part = part;
+    ra.dx = xa.dx;
+    ra.part_stride = xa.part_stride;
+    ra.count = (int64_t)rows * p.H;
+    ra.splits = p.splits;
+    ra.dx_fp32 = xa.dx_fp32;
+    ra.accumulate = xa.accumulate;
+    FLCE_LAUNCH(mark(h, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
+    FLCE_LAUNCH(flce::launch_dx_reduce(ra, st));
   }
 
+  flce::DwArgs wa{};
+  wa.g = z;
+  wa.x = x_c;
+  wa.dW = dW;
+  wa.ldg = p.Vp;
+  wa.rows = rows;
+  wa.H = (int)p.H;
+  wa.V = (int)p.V;
+  wa.tiles_m = p.tiles_v;
+  wa.tiles_n = p.tiles_h;
+  wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
+  wa.accumulate = s > 0 || o.accumulate;
+  FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
+                   zbytes + (double)rows * p.H * b_in + VH * b_dw * (wa.accumulate ? 2.0 : 1.0), st));
+  FLCE_LAUNCH(flce::launch_dw(in, wa, st));
+  return FLCE_OK;
+}
+
+flce_status_t finalize_loss(flce_handle_s* h, const Plan& p, float* loss, hipStream_t st) {
+  char* ws = static_cast<char*>(h->ws);
   flce::FinalizeArgs fa{};
-  fa.loss_rows = loss_rows;
+  fa.loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   fa.loss = loss;
   fa.n = p.N;
-  fa.scale = scale;
+  fa.scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
   FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
   FLCE_LAUNCH(flce::launch_finalize(fa, st));
+  return FLCE_OK;
+}
+
+flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
+                          const int64_t* t, float* loss, void* dx, void* dW, float* lse_out,
+                          hipStream_t st) {
+  const flce_config_t& cfg = h->cfg;
+  const size_t es = in_size(cfg);
+  const size_t dx_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(static_cast<char*>(h->ws) + p.off_lse);
+  flce_status_t r = launch_scale(h, p, o, t, st);
+  if (r != FLCE_OK) return r;
+  for (int64_t s = 0; s < p.N; s += p.C) {
+    const int rows = (int)std::min(p.C, p.N - s);
+    const DxOut dxo{o.grads ? static_cast<char*>(dx) + (size_t)s * p.H * dx_es : nullptr,
+                    cfg.dx_dtype == FLCE_FP32, o.accumulate};
+    r = chunk_flce(h, p, o, s, rows, static_cast<const char*>(x) + (size_t)s * p.H * es, W, t, lse, dxo, dW, st);
+    if (r != FLCE_OK) return r;
+  }
+  r = finalize_loss(h, p, loss, st);
+  if (r != FLCE_OK) return r;
+  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  return FLCE_OK;
+}
+
+// RMSNorm in front of the head, per chunk: x_c = rmsnorm(h_c) into the workspace, the FLCE
+// chunk with its dx rows in an fp32 workspace buffer, then dh rows and dgamma partials from
+// them; dgamma is summed in fp32 across chunks and written (or added) in its dtype at the end.
+flce_status_t run_rmsnorm(flce_handle_s* h, const Plan& p, const Opts& o, const void* hid, const void* gamma,
+                          float eps, const void* W, const int64_t* t, float* loss, void* dh, void* dgamma,
+                          void* dW, float* lse_out, hipStream_t st) {
+  const flce_config_t& cfg = h->cfg;
+  const In in = cfg.in_dtype == FLCE_BF16 ? In::BF16 : In::FP32;
+  const size_t es = in_size(cfg);
+  const size_t dh_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
+  char* ws = static_cast<char*>(h->ws);
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
+  void* xc = ws + p.off_xc;
+  float* dxc = reinterpret_cast<float*>(ws + p.off_dxc);
+  float* rstd = reinterpret_cast<float*>(ws + p.off_rstd);
+  float* rpart = reinterpret_cast<float*>(ws + p.off_rpart);
+  const bool dg32 = cfg.dw_dtype == FLCE_FP32;
+  float* dg_acc = dg32 ? static_cast<float*>(dgamma) : reinterpret_cast<float*>(ws + p.off_dgacc);
+  const double H = (double)p.H;
+  flce_status_t r = launch_scale(h, p, o, t, st);
+  if (r != FLCE_OK) return r;
+  if (o.grads && !(dg32 && o.accumulate)) {   // fp32 dgamma is its own accumulator
+    flce::FillArgs zg{dg_acc, p.H};
+    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * H, st));
+    FLCE_LAUNCH(flce::launch_fill_zero(zg, st));
+  }
+  for (int64_t s = 0; s < p.N; s += p.C) {
+    const int rows = (int)std::min(p.C, p.N - s);
+    const void* hc = static_cast<const char*>(hid) + (size_t)s * p.H * es;
+    flce::RmsFwdArgs fa{hc, gamma, xc, rstd, rows, (int)p.H, eps};
+    FLCE_LAUNCH(mark(h, K_RMS_FWD, 0.0, (2.0 * rows + 1.0) * H * (double)es + 4.0 * rows, st));
+    FLCE_LAUNCH(flce::launch_rms_fwd(in, fa, st));
+    r = chunk_flce(h, p, o, s, rows, xc, W, t, lse, DxOut{dxc, true, false}, dW, st);
+    if (r != FLCE_OK) return r;
+    if (!o.grads) continue;
+    const int nblk = (int)cdiv(rows, flce::kRmsRowsPerBlock);
+    flce::RmsBwdArgs ba{dxc, hc, gamma, rstd, static_cast<char*>(dh) + (size_t)s * p.H * dh_es, rpart,
+                        rows, (int)p.H, cfg.dx_dtype == FLCE_FP32, o.accumulate};
+    FLCE_LAUNCH(mark(h, K_RMS_BWD, 0.0, rows * H * (4.0 + (double)es + (double)dh_es) + nblk * H * 4.0, st));
+    FLCE_LAUNCH(flce::launch_rms_bwd(in, ba, st));
+    flce::RmsReduceArgs ra{rpart, dg_acc, nblk, (int)p.H};
+    FLCE_LAUNCH(mark(h, K_RMS_REDUCE, 0.0, (nblk + 2.0) * H * 4.0, st));
+    FLCE_LAUNCH(flce::launch_rms_reduce(ra, st));
+  }
+  if (o.grads && !dg32) {
+    flce::CastArgs cg{dg_acc, dgamma, p.H, o.accumulate};
+    FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * H, st));
+    FLCE_LAUNCH(flce::launch_cast_bf16(cg, st));
+  }
+  r = finalize_loss(h, p, loss, st);
+  if (r != FLCE_OK) return r;
   FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
   return FLCE_OK;
 }
@@ -530,6 +621,31 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
   return FLCE_OK;
 }
 
+
+// Options in launch form; false for malformed ones.
+bool parse_options(const flce_options_t* opt, Opts& o) {
+  if (opt == nullptr) return true;
+  if ((opt->reduction != FLCE_MEAN && opt->reduction != FLCE_SUM) ||
+      (opt->flags & ~(FLCE_ACCUMULATE | FLCE_FORWARD_ONLY)) != 0 ||
+      ((opt->flags & FLCE_ACCUMULATE) && (opt->flags & FLCE_FORWARD_ONLY)) || opt->ignore_on < 0 ||
+      opt->ignore_on > 1 || opt->reserved != 0)
+    return false;
+  o.sum = opt->reduction == FLCE_SUM;
+  o.accumulate = (opt->flags & FLCE_ACCUMULATE) != 0;
+  o.grads = (opt->flags & FLCE_FORWARD_ONLY) == 0;
+  o.ign = flce::Ignore{opt->ignore_index, opt->ignore_on};
+  return true;
+}
+
+// Largest H of the RMSNorm path: its backward keeps one fp32 dgamma row of H in LDS.
+constexpr int64_t kRmsMaxH = 32768;
+
+flce_status_t validate_rmsnorm(const flce_config_t& cfg, int64_t H, float eps) {
+  if (!(eps >= 0.f) || eps > 1e30f) return FLCE_ERR_INVALID_ARG;   // rejects NaN too
+  if (cfg.variant != FLCE_CHUNKED || H > kRmsMaxH) return FLCE_ERR_UNSUPPORTED;
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -592,12 +708,9 @@ size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, in
 size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
                                 const flce_options_t* opt) {
   if (h == nullptr || validate_sizes(h->cfg, N, H, V, chunk) != FLCE_OK) return 0;
-  bool grads = true;
-  if (opt != nullptr) {
-    if ((opt->flags & ~(FLCE_ACCUMULATE | FLCE_FORWARD_ONLY)) != 0) return 0;
-    grads = (opt->flags & FLCE_FORWARD_ONLY) == 0;
-  }
-  return make_plan(h->cfg, N, H, V, chunk, grads).total;
+  Opts o;
+  if (!parse_options(opt, o)) return 0;
+  return make_plan(h->cfg, N, H, V, chunk, o.grads).total;
 }
 
 flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk) {
@@ -612,17 +725,7 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
                                         int64_t chunk, const flce_options_t* opt, float* loss, void* dx,
                                         void* dW, float* lse, void* stream) {
   Opts o;
-  if (opt != nullptr) {
-    if ((opt->reduction != FLCE_MEAN && opt->reduction != FLCE_SUM) ||
-        (opt->flags & ~(FLCE_ACCUMULATE | FLCE_FORWARD_ONLY)) != 0 ||
-        ((opt->flags & FLCE_ACCUMULATE) && (opt->flags & FLCE_FORWARD_ONLY)) || opt->ignore_on < 0 ||
-        opt->ignore_on > 1 || opt->reserved != 0)
-      return FLCE_ERR_INVALID_ARG;
-    o.sum = opt->reduction == FLCE_SUM;
-    o.accumulate = (opt->flags & FLCE_ACCUMULATE) != 0;
-    o.grads = (opt->flags & FLCE_FORWARD_ONLY) == 0;
-    o.ign = flce::Ignore{opt->ignore_index, opt->ignore_on};
-  }
+  if (!parse_options(opt, o)) return FLCE_ERR_INVALID_ARG;
   if (h == nullptr || x == nullptr || W == nullptr || targets == nullptr || loss == nullptr ||
       (o.grads && (dx == nullptr || dW == nullptr)))
     return FLCE_ERR_INVALID_ARG;
@@ -641,6 +744,44 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (p.fused) return run_fused(h, p, o, x, W, targets, loss, dx, dW, lse, st);
   return run_chunked(h, p, o, x, W, targets, loss, dx, dW, lse, st);
+}
+
+
+size_t flce_rmsnorm_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,
+                                    const flce_options_t* opt) {
+  Opts o;
+  if (h == nullptr || !parse_options(opt, o) || validate_sizes(h->cfg, N, H, V, chunk) != FLCE_OK ||
+      validate_rmsnorm(h->cfg, H, 0.f) != FLCE_OK)
+    return 0;
+  return make_plan(h->cfg, N, H, V, chunk, o.grads, true).total;
+}
+
+flce_status_t flce_rmsnorm_forward_backward(flce_handle_t h, const void* hidden, const void* gamma, float eps,
+                                            const void* W, const int64_t* targets, int64_t N, int64_t H,
+                                            int64_t V, int64_t chunk, const flce_options_t* opt, float* loss,
+                                            void* dhidden, void* dgamma, void* dW, float* lse, void* stream) {
+  Opts o;
+  if (!parse_options(opt, o)) return FLCE_ERR_INVALID_ARG;
+  if (h == nullptr || hidden == nullptr || gamma == nullptr || W == nullptr || targets == nullptr ||
+      loss == nullptr || (o.grads && (dhidden == nullptr || dgamma == nullptr || dW == nullptr)))
+    return FLCE_ERR_INVALID_ARG;
+  flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
+  if (v != FLCE_OK) return v;
+  v = validate_rmsnorm(h->cfg, H, eps);
+  if (v != FLCE_OK) return v;
+  if (!aligned16(hidden) || !aligned16(gamma) || !aligned16(W) ||
+      (o.grads && (!aligned16(dhidden) || !aligned16(dgamma) || !aligned16(dW))) ||
+      (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return FLCE_ERR_UNSUPPORTED;
+  if (o.grads && (dhidden == hidden || dW == W || dgamma == gamma)) return FLCE_ERR_INVALID_ARG;
+  const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads, true);
+  const flce_status_t ws = ensure_workspace(h, p.total);
+  if (ws != FLCE_OK) return ws;
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  return run_rmsnorm(h, p, o, hidden, gamma, eps, W, targets, loss, dhidden, dgamma, dW, lse,
+                     static_cast<hipStream_t>(stream));
 }
 
 flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,

@@ -142,6 +142,37 @@ struct CastArgs {       // fp32 -> bf16, round to nearest even
   int accumulate;       // 1: dst = bf16(dst + src)
 };
 
+// RMSNorm in front of the head, per token chunk: x = h * rstd * gamma with
+// rstd = 1 / sqrt(mean(h^2) + eps), and its backward from the chunk's fp32 dL/dx.
+struct RmsFwdArgs {
+  const void* h;        // chunk's first row [rows][H] (in-type)
+  const void* gamma;    // [H] (in-type)
+  void* x;              // [rows][H] (in-type)
+  float* rstd;          // [rows]
+  int rows, H;
+  float eps;
+};
+
+constexpr int kRmsRowsPerBlock = 8;   // rows whose dgamma contributions one backward block sums
+
+struct RmsBwdArgs {
+  const float* dx;      // [rows][H] fp32
+  const void* h;        // [rows][H] (in-type)
+  const void* gamma;    // [H] (in-type)
+  const float* rstd;    // [rows]
+  void* dh;             // chunk's first row of dh [rows][H]
+  float* part;          // [ceil(rows / kRmsRowsPerBlock)][H] fp32 dgamma partials
+  int rows, H;
+  int dh_fp32;
+  int accumulate;       // 1: dh += result
+};
+
+struct RmsReduceArgs {  // acc[k] += sum over b of part[b][k], b in order
+  const float* part;
+  float* acc;
+  int nblk, H;
+};
+
 hipError_t launch_logits(In in, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_dlogits(In in, const DlogitsArgs& a, hipStream_t s);
@@ -153,5 +184,8 @@ hipError_t launch_fused_bwd(const FusedArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(const FillArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);
+hipError_t launch_rms_fwd(In in, const RmsFwdArgs& a, hipStream_t s);
+hipError_t launch_rms_bwd(In in, const RmsBwdArgs& a, hipStream_t s);
+hipError_t launch_rms_reduce(const RmsReduceArgs& a, hipStream_t s);
 
 }  // namespace flce
