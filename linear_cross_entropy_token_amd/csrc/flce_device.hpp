@@ -7,17 +7,17 @@
 //    by v_mfma_f32_32x32x16_bf16 (bf16 inputs) or v_mfma_f32_32x32x2_f32
 //    (fp32 inputs);
 //  * the contraction is walked in k-slices of 128 bytes per operand row
-//    (64 bf16 / 32 fp32, one full cache line per k-major row) through a
-//    2-stage LDS ring (2 x 64 KiB; the logits GEMM uses all 160 KiB, see
-//    gemm_tile_deep_c): operand tiles are copied HBM -> LDS by buffer_load
-//    ... lds (direct-to-LDS DMA, no VGPR staging), issued one slice ahead of
-//    the MFMAs that consume them; out-of-range rows/columns come back as
-//    zeros from the buffer range check, so ragged edges need no branches.
-//    (Measured on MI355X: full-line requests with 2 stages beat half-line
-//    requests with 4 stages of 32 KiB on all three GEMMs.)
-//  * the two waves of each SIMD run a ping-pong schedule (gemm_tile): one
-//    multiplies a whole k-slice from registers while the other reads the
-//    next fragments from LDS and issues copies;
+//    (64 bf16 / 32 fp32, one full cache line per k-major row) through an
+//    LDS ring: operand tiles are copied HBM -> LDS by buffer_load ... lds
+//    (direct-to-LDS DMA, no VGPR staging) ahead of the MFMAs that consume
+//    them; out-of-range rows/columns come back as zeros from the buffer
+//    range check, so ragged edges need no branches.  (Measured on MI355X:
+//    full-line requests beat half-line requests with more stages.)
+//  * the two waves of each SIMD run a ping-pong schedule: one multiplies a
+//    whole k-slice from registers while the other reads the next fragments
+//    from LDS and issues copies.  gemm_tile uses a 2-stage ring (2 x 64 KiB);
+//    gemm_tile_balanced uses all 160 KiB (3 slots for one operand, 2 for the
+//    other) so that each phase carries half a slice of copies.
 //  * an operand stored with the contraction index contiguous ("k-major": x
 //    and W for the logits, G for dx) is kept k-major in LDS and read with
 //    ds_read_b128; an operand whose contraction index is the ROW ("mn-major":
@@ -156,10 +156,21 @@ struct Operand {
   // Copies the slice starting at contraction index k0 (k < k_end valid) into lds_op.
   // Offsets are 32-bit: every valid byte of the buffer lies below 2^32.
   __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave) const {
-    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int b = wave * BPW + i;                  // 1 KiB block of the operand's stage
+    for (int i = 0; i < BPW; ++i) issue_block(lds_op, k0, k_end, wave * BPW + i);
+  }
+
+  // Blocks vw * N .. vw * N + N - 1 of the slice (one wave of a group of 4 copying the whole slice).
+  template <int N>
+  __device__ __forceinline__ void issue_part(char* lds_op, int k0, int k_end, int vw) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) issue_block(lds_op, k0, k_end, vw * N + i);
+  }
+
+  // 1 KiB block b (0 .. 8 BPW - 1) of the slice at k0.
+  __device__ __forceinline__ void issue_block(char* lds_op, int k0, int k_end, int b) const {
+    const int lane = threadIdx.x & 63;
+    {
       int mn, kpos;
       uint32_t off;
       if constexpr (KMAJOR) {
@@ -187,7 +198,15 @@ struct Operand {
 
 // Fragment of one 32-index block for k-step s (16 bf16 / 8 fp32 k-values; kSteps per slice):
 // lane l supplies index mnb + l % 32 and the k-values 8 (l / 32) .. +7 (bf16) / 4 (l / 32) .. +3 (fp32).
-template <typename T, bool KMAJOR>
+//
+// ASM (bf16 mn-major only): issue the transposing reads as inline assembly.  The compiler
+// treats the transposing-read builtin as possibly aliasing every direct-to-LDS copy still in
+// flight and inserts a wait for all of them (vmcnt(0)) before it, which stalls a wave that
+// has just issued the next slice's copies for the whole copy latency (measured: dx 15%, dW 8%
+// slower).  The ping-pong loops order copies and reads with their own waits and barriers and
+// wait for these reads (lgkmcnt(0)) before the MFMAs use them, so the asm form is exact there;
+// loops that rely on compiler-inserted waits must use the builtin.
+template <typename T, bool KMAJOR, bool ASM = false>
 __device__ __forceinline__ u32x4 read_frag(const char* op, int mnb, int s, int lane) {
   if constexpr (KMAJOR) {
     const int row = mnb + (lane & 31);
@@ -200,6 +219,13 @@ __device__ __forceinline__ u32x4 read_frag(const char* op, int mnb, int s, int l
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const lds_i16x4* p0 = (const lds_i16x4*)(op + r * 512 + ((g ^ swz_mn(r)) << 5) + byte);
     const lds_i16x4* p1 = (const lds_i16x4*)(op + (r + 4) * 512 + ((g ^ swz_mn(r + 4)) << 5) + byte);
+    if constexpr (ASM) {   // p1 = p0 + 4 rows: swz_mn depends on r % 4 only
+      const uint32_t a0 = (uint32_t)(uintptr_t)p0;
+      u32x2 l2, h2;
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(l2) : "v"(a0));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(h2) : "v"(a0));
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
@@ -242,6 +268,13 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Waits for this wave's LDS reads; no instruction moves across it.
+__device__ __forceinline__ void lgkm_wait() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // acc[i][j] += sum over k in [k_begin, k_end) of C[col 32i + ..][k] * R[row 32j + ..][k] for the
 // wave's 128 x 64 part of the tile.  C and R fill their halves of each LDS stage.
 //
@@ -251,9 +284,10 @@ __device__ __forceinline__ void phase_barrier() {
 // copies, so the matrix core never waits for the LDS pipe of its own wave.  With phases
 // numbered from 0, waves 0-3 read slice kt in phase 2kt and multiply in 2kt+1; waves 4-7
 // read it in 2kt+1 and multiply in 2kt+2.  Slice kt+1 is copied into the other stage
-// during phases 2kt and 2kt+1 (each wave copies its share at the start of phase 2kt; both
-// readers of the slice it replaces finished by phase 2kt-1) and every wave waits for its
-// copies at the end of phase 2kt+1.  There are 2 nk + 1 phases per tile.
+// during phase 2kt (both readers of the slice it replaces finished by phase 2kt-1): waves
+// 0-3 copy their share after reading slice kt, waves 4-7 before multiplying slice kt-1, and
+// every wave waits for its copies at the end of phase 2kt+1.  There are 2 nk + 1 phases per
+// tile.
 template <typename T, class OpC, class OpR>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C, const OpR& R,
                                           int k_begin, int k_end) {
@@ -283,9 +317,9 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-      for (int i = 0; i < kColBlocks; ++i) fa[s][i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
+      for (int i = 0; i < kColBlocks; ++i) fa[s][i] = read_frag<T, OpC::kKMajor, true>(st, colb + 32 * i, s, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[s][j] = read_frag<T, OpR::kKMajor>(st + kOpBytes, rowb + 32 * j, s, lane);
+      for (int j = 0; j < 4; ++j) fb[s][j] = read_frag<T, OpR::kKMajor, true>(st + kOpBytes, rowb + 32 * j, s, lane);
     }
   };
   auto multiply = [&]() {
@@ -300,9 +334,10 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
   phase_barrier<true, false>();                 // slice 0 resident
   if (wave < kWaves / 2) {
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) issue(kt + 1);           // phase 2kt
-      read(kt);
-      phase_barrier<false, true>();
+      read(kt);                                 // phase 2kt
+      lgkm_wait();
+      if (kt + 1 < nk) issue(kt + 1);
+      phase_barrier<false, false>();
       multiply();                               // phase 2kt + 1
       phase_barrier<true, false>();
     }
@@ -321,38 +356,37 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
   __syncthreads();   // LDS free for the epilogue
 }
 
-// Joins the barrier once this wave's copies have landed, except (keep4) the 4 it issued last.
-template <bool LGKM>
-__device__ __forceinline__ void vm_barrier_keep4(bool keep4) {
-  static_assert(kBlocksPerWave == 4, "one operand's copies per wave and slice");
+// Joins the barrier once this wave's copies have landed, except (keep8) the 8 it issued last.
+__device__ __forceinline__ void vm_barrier_keep8(bool keep8) {
   __builtin_amdgcn_sched_barrier(0);
-  if (keep4) {
-    if constexpr (LGKM) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-  } else {
-    if constexpr (LGKM) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  }
+  if (keep8) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// gemm_tile with all 160 KiB of LDS: the column operand in a 3-slot ring, copied two slices
-// ahead, the row operand in a 2-slot ring, copied one slice ahead, so the column operand's
-// copies get four phases to land instead of two.  Slot of C(j): j % 3 (its previous occupant
-// C(j-3) was last read in phase 2j-5; C(j) is issued in phase 2j-4); slot of R(j): j % 2
-// (previous occupant read in phase 2j-3; issued in phase 2j-2).  Each wave issues R(kt+1)
-// before C(kt+2), so waiting for slice kt+1 leaves only C(kt+2)'s 4 copies in flight.
-// Measured: the logits GEMM (column operand W streaming from HBM) 3.5% faster; dx and dW are
-// slower with either operand deepened, so they keep gemm_tile.
+// gemm_tile over all 160 KiB of LDS: the column operand C in a 3-slot ring, the row operand R
+// in a 2-slot ring, and the copies of each slice split between the two wave groups so that
+// every phase carries half a slice of them, issued by the group that is reading (its matrix
+// core is busy with the other group's MFMAs).  Phases as in gemm_tile: waves 0-3 read slice m
+// in phase 2m and multiply it in 2m+1, waves 4-7 read it in 2m+1 and multiply it in 2m+2.
+//   * waves 0-3, after reading slice m, copy R(m+1) (8 blocks each) into R slot (m+1) % 2,
+//     whose previous slice m-1 was last read in phase 2m-1; they wait for it at the end of
+//     phase 2m+1, one phase before its first reader;
+//   * waves 4-7, after reading slice m, copy C(m+2) (8 blocks each) into C slot (m+2) % 3,
+//     whose previous slice m-1 was last read in phase 2m-1; they wait for it at the end of
+//     phase 2m+3 (keeping only the newer C(m+3) in flight), so C's copies get two phases.
+// Measured against gemm_tile at the Llama-3 chunk: logits -11%, dx -3%; dW (both operands
+// read with transposing reads, so its read phases are the longest) stays on gemm_tile.
 constexpr int kDeepRingBytes = 5 * kOpBytes;   // 160 KiB
 template <typename T, class OpC, class OpR>
-__device__ __forceinline__ void gemm_tile_deep_c(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C,
-                                                 const OpR& R, int k_begin, int k_end) {
-  static_assert(kWaves == 8, "the ping-pong schedule pairs the waves of a SIMD");
+__device__ __forceinline__ void gemm_tile_balanced(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C,
+                                                   const OpR& R, int k_begin, int k_end) {
+  static_assert(kWaves == 8 && kBlocksPerWave == 4, "two groups of 4 waves; 8 blocks per wave copy a slice");
   constexpr int BK = slice_k<T>();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vw = wave & 3;                       // position inside the wave group
   const int rowb = (wave / kWaveCols) * 128;
   const int colb = (wave % kWaveCols) * (kTile / kWaveCols);
 #pragma unroll
@@ -363,18 +397,18 @@ __device__ __forceinline__ void gemm_tile_deep_c(f32x16 (&acc)[kColBlocks][4], c
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int nk = (k_end - k_begin + BK - 1) / BK;
   char* ringR = smem + 3 * kOpBytes;
-  auto issue_r = [&](int kt) { if (kt < nk) R.issue(ringR + (kt & 1) * kOpBytes, k_begin + kt * BK, k_end, wave); };
-  auto issue_c = [&](int kt) { if (kt < nk) C.issue(smem + (kt % 3) * kOpBytes, k_begin + kt * BK, k_end, wave); };
+  auto slot_c = [&](int kt) { return smem + (kt % 3) * kOpBytes; };
+  auto slot_r = [&](int kt) { return ringR + (kt & 1) * kOpBytes; };
   u32x4 fa[kSteps][kColBlocks], fb[kSteps][4];
   auto read = [&](int kt) {
-    const char* sc = smem + (kt % 3) * kOpBytes;
-    const char* sr = ringR + (kt & 1) * kOpBytes;
+    const char* sc = slot_c(kt);
+    const char* sr = slot_r(kt);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
-      for (int i = 0; i < kColBlocks; ++i) fa[s][i] = read_frag<T, OpC::kKMajor>(sc, colb + 32 * i, s, lane);
+      for (int i = 0; i < kColBlocks; ++i) fa[s][i] = read_frag<T, OpC::kKMajor, true>(sc, colb + 32 * i, s, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[s][j] = read_frag<T, OpR::kKMajor>(sr, rowb + 32 * j, s, lane);
+      for (int j = 0; j < 4; ++j) fb[s][j] = read_frag<T, OpR::kKMajor, true>(sr, rowb + 32 * j, s, lane);
     }
   };
   auto multiply = [&]() {
@@ -385,30 +419,31 @@ __device__ __forceinline__ void gemm_tile_deep_c(f32x16 (&acc)[kColBlocks][4], c
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
   };
-  issue_r(0);
-  issue_c(0);
-  issue_c(1);
-  vm_barrier_keep4<false>(1 < nk);             // slice 0 resident; C(1) may be in flight
+  if (nk > 0) {                                  // slice 0: every wave copies its share
+    C.issue(slot_c(0), k_begin, k_end, wave);
+    R.issue(slot_r(0), k_begin, k_end, wave);
+  }
   if (wave < kWaves / 2) {
-    for (int kt = 0; kt < nk; ++kt) {
-      issue_r(kt + 1);                          // phase 2kt
-      issue_c(kt + 2);
-      read(kt);
-      phase_barrier<false, true>();
-      multiply();                               // phase 2kt + 1
-      vm_barrier_keep4<false>(kt + 2 < nk);     // slice kt+1 resident
+    vm_barrier_keep8(false);                     // slice 0 resident
+    for (int m = 0; m < nk; ++m) {
+      read(m);                                   // phase 2m
+      lgkm_wait();
+      if (m + 1 < nk) R.template issue_part<8>(slot_r(m + 1), k_begin + (m + 1) * BK, k_end, vw);
+      phase_barrier<false, false>();
+      multiply();                                // phase 2m + 1
+      vm_barrier_keep8(false);                   // R(m+1) resident
     }
-    phase_barrier<false, false>();              // phase 2nk
+    phase_barrier<false, false>();               // phase 2nk
   } else {
-    issue_r(1);                                 // phase 0
-    issue_c(2);
-    phase_barrier<false, false>();
-    for (int kt = 0; kt < nk; ++kt) {
-      read(kt);                                 // phase 2kt + 1
-      vm_barrier_keep4<true>(kt + 2 < nk);
-      issue_r(kt + 2);                          // phase 2kt + 2
-      issue_c(kt + 3);
-      multiply();
+    if (1 < nk) C.template issue_part<8>(slot_c(1), k_begin + BK, k_end, vw);
+    vm_barrier_keep8(1 < nk);                    // slice 0 resident; C(1) may be in flight
+    phase_barrier<false, false>();               // phase 0
+    for (int m = 0; m < nk; ++m) {
+      read(m);                                   // phase 2m + 1
+      lgkm_wait();
+      if (m + 2 < nk) C.template issue_part<8>(slot_c(m + 2), k_begin + (m + 2) * BK, k_end, vw);
+      vm_barrier_keep8(m + 2 < nk);              // C(m+1) resident
+      multiply();                                // phase 2m + 2
       phase_barrier<false, false>();
     }
   }

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
     rel = (d >= 0 && d < kTile) ? (int)d : -1;
   }
   f32x16 acc[kColBlocks][4];
-  gemm_tile_deep_c<T>(acc, smem, C, R, 0, a.H);
+  gemm_tile_balanced<T>(acc, smem, C, R, 0, a.H);
 
   const Frag f = frag_coords();
   // [2][kWaveCols][kTile]: per column-wave max, then sum; then the target column per row.  The
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const int tiles = a.tiles_m * a.tiles_n;
   const int L = xcd_remap(blockIdx.x, tiles * a.splits);
   const int split = L / tiles;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES));
   R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES));
   f32x16 acc[kColBlocks][4];
-  gemm_tile<T>(acc, smem, C, R, ks, ke);
+  gemm_tile_balanced<T>(acc, smem, C, R, ks, ke);
 
   const Frag f = frag_coords();
 #pragma unroll
