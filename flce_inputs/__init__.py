@@ -58,6 +58,12 @@ WORKLOADS: Dict[str, Workload] = {
                             "Qwen3 vocab, bf16, N=16384 (4x4096) H=4096 V=151936, Zipf(1.1) targets"),
     "long_context": Workload("long_context", 131072, 4096, 128256, "bf16", "uniform", 4096, 5,
                              "long context, bf16, N=131072 (1x128K) H=4096 V=128256"),
+    # one GPU's share of the Llama-3 workload when it is split 8 ways (the path itself runs on one
+    # GPU): by tokens (data parallel: N/8 rows, all of W) or by vocabulary (V/8 rows of W, all N)
+    "llama3_dp8_share": Workload("llama3_dp8_share", 2048, 4096, 128256, "bf16", "uniform", 2048, 6,
+                                 "Llama-3 vocab, token shard of 8: N=2048 H=4096 V=128256"),
+    "llama3_tp8_share": Workload("llama3_tp8_share", 16384, 4096, 16032, "bf16", "uniform", 4096, 7,
+                                 "Llama-3 vocab, vocabulary shard of 8: N=16384 H=4096 V=16032"),
 }
 
 

@@ -71,6 +71,13 @@ def load_library() -> ctypes.CDLL:
     path = library_path()
     if not os.path.exists(path):
         raise OSError(f"{path} is missing: build it with `python -m linear_cross_entropy_token_amd.build`")
+    # One HIP runtime per process: torch ships its own libamdhip64, and a process that loads
+    # this library first and torch afterwards ends up with two runtimes that fail each other's
+    # calls.  Loading torch first makes the library bind to torch's runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.flce_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(vp)]

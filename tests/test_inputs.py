@@ -65,3 +65,7 @@ def test_workload_table():
     assert (w.N, w.H, w.V, w.dtype) == (16384, 4096, 128256, "bf16")
     assert WORKLOADS["qwen3_vocab"].targets == "zipf"
     assert WORKLOADS["tiny_fp32"].dtype == "fp32"
+    # one GPU's shares of the Llama-3 workload split 8 ways: by tokens and by vocabulary
+    dp, tp = WORKLOADS["llama3_dp8_share"], WORKLOADS["llama3_tp8_share"]
+    assert (dp.N * 8, dp.H, dp.V) == (w.N, w.H, w.V)
+    assert (tp.N, tp.H, tp.V * 8) == (w.N, w.H, w.V)

@@ -150,7 +150,8 @@ def _sample_rows(N, C):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["llama2_vocab", "llama3_vocab", "qwen3_vocab", "long_context"])
+@pytest.mark.parametrize("name", ["llama2_vocab", "llama3_vocab", "qwen3_vocab", "long_context",
+                                  "llama3_dp8_share", "llama3_tp8_share"])
 def test_full_size_sampled(name):
     """Full workload size, benchmark launch configuration (bf16 outputs): sampled rows of lse
     and dx against the oracle, and the loss against its expectation.  Then the same launch
