@@ -185,16 +185,28 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
   const float ninf = -__builtin_inff();
   float M = ninf, S = 0.f;
   if (r < a.rows) {
-    for (int j = part; j < a.tiles_n; j += 8) {
-      const float m = a.pm[(int64_t)j * a.pstride + r];
-      const float s = a.ps[(int64_t)j * a.pstride + r];
-      if (m == ninf) continue;
-      if (m > M) {
-        S = S * fast_exp(M - m) + s;
-        M = m;
-      } else {
-        S += s * fast_exp(m - M);
+    // kU tiles per round, loaded before any of them is merged, so that a round costs one
+    // memory latency instead of kU
+    constexpr int kU = 8;
+    for (int j0 = part; j0 < a.tiles_n; j0 += 8 * kU) {
+      float m[kU], s[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int j = j0 + 8 * u;
+        const bool in = j < a.tiles_n;
+        m[u] = in ? a.pm[(int64_t)j * a.pstride + r] : ninf;
+        s[u] = in ? a.ps[(int64_t)j * a.pstride + r] : 0.f;
       }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) Mn = fmaxf(Mn, m[u]);
+      if (Mn == ninf) continue;                     // nothing but empty partials so far
+      float Sn = M == ninf ? 0.f : S * fast_exp(M - Mn);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (m[u] != ninf) Sn += s[u] * fast_exp(m[u] - Mn);
+      M = Mn;
+      S = Sn;
     }
   }
   sm[part][rl] = M;
