@@ -44,6 +44,12 @@ SMALL = [
     ("bf16_H264", 520, 264, 1300, "bf16", 200, None),
     ("bf16_H264_fp32_grads", 520, 264, 1300, "bf16", 200, "fp32"),
     ("fp32_H264", 200, 264, 900, "fp32", 64, None),
+    # contractions of one or two k-slices in both LDS rings: H = 32 / 64 / 128 for the logits,
+    # a vocabulary of one or two tiles for dx, chunks of 40 / 64 / 96 / 100 tokens for dW
+    ("bf16_V50_H64", 64, 64, 50, "bf16", 0, None),
+    ("bf16_V300_H128_N100", 100, 128, 300, "bf16", 0, None),
+    ("fp32_V50_H32", 40, 32, 50, "fp32", 0, None),
+    ("bf16_C96_V700", 300, 192, 700, "bf16", 96, None),
 ]
 
 
