@@ -361,6 +361,8 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
 
   flce::DlogitsArgs ga{};
   ga.z = z;
+  ga.pm = pm;
+  ga.pstride = (int)p.C;
   ga.lse = lse + s;
   ga.t = t + s;
   ga.ldz = p.Vp;
@@ -368,7 +370,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   ga.V = (int)p.V;
   ga.ign = o.ign;
   ga.scale = scale;
-  FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes, st));
+  FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes + 4.0 * rows * p.tiles_v, st));
   FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
 
   flce::DxArgs xa{};

@@ -64,7 +64,9 @@ struct CombineArgs {
 };
 
 struct DlogitsArgs {
-  void* z;              // [rows][ldz] in-type, overwritten with G
+  void* z;              // [rows][ldz] in-type: z - M per 256-column tile, overwritten with G
+  const float* pm;      // [ldz / 256][pstride] the tile maxima M
+  int pstride;
   const float* lse;
   const int64_t* t;
   int64_t ldz;

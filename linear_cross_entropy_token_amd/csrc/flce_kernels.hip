@@ -122,26 +122,38 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
             hit = hit || h;
           }
       if (hit) a.zt[grow] = zsel;
-      if (Z != nullptr) {   // null: statistics-only pass
-#pragma unroll
-        for (int i = 0; i < kColBlocks; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int c0 = f.col0(i, q);
-            if constexpr (ES == 2) {
-              const int c = c0 >> 3;
-              *reinterpret_cast<u32x2*>(smem + row * 512 + ((c ^ (row & 31)) << 4) + 8 * (f.lane >> 5)) =
-                  u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                        pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-            } else {
-              *reinterpret_cast<f32x4*>(Z + (int64_t)grow * a.ldz + n0 + c0) =
-                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            }
-          }
-      }
     }
   }
-  phase_barrier<false, true>();   // partials and the z tile visible in LDS
+  phase_barrier<false, true>();   // per-wave row statistics visible in LDS
+  if (Z != nullptr) {   // null: statistics-only pass
+    // The buffer holds z - M, M the row's maximum over this 256-column tile (the tile's LSE
+    // partial), so that the values that carry the softmax mass sit near zero, where bf16 is
+    // finest: rounding then perturbs exp(z - lse) by ~2^-9 relatively at any logit scale,
+    // where rounding z itself would perturb it by |z| 2^-9 (3% at |z| = 40).
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = f.row(j);
+      float M = red[row];
+#pragma unroll
+      for (int w = 1; w < kWaveCols; ++w) M = fmaxf(M, red[w * kTile + row]);
+#pragma unroll
+      for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = f.col0(i, q);
+          const f32x4 v{acc[i][j][4 * q] - M, acc[i][j][4 * q + 1] - M, acc[i][j][4 * q + 2] - M,
+                        acc[i][j][4 * q + 3] - M};
+          if constexpr (ES == 2) {
+            const int c = c0 >> 3;
+            *reinterpret_cast<u32x2*>(smem + row * 512 + ((c ^ (row & 31)) << 4) + 8 * (f.lane >> 5)) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else if (m0 + row < a.rows) {
+            *reinterpret_cast<f32x4*>(Z + (int64_t)(m0 + row) * a.ldz + n0 + c0) = v;
+          }
+        }
+    }
+  }
+  phase_barrier<false, true>();   // the z tile visible in LDS
   if constexpr (ES == 2) {
     if (Z != nullptr) {   // full 512-byte rows of z: 2 rows per 1 KiB block, 16 blocks per wave
       const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,7 +256,8 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(idx / per_row);
     const int c0 = (int)(idx - (int64_t)r * per_row) * E;
-    const float l = a.lse[r];
+    // the buffer holds z - M (M: the row's maximum over the 256-column tile, its LSE partial)
+    const float l = a.lse[r] - a.pm[(int64_t)(c0 / kTile) * a.pstride + r];
     const int64_t tv = a.t[r];
     const bool counted = !a.ign.skip(tv);   // an ignored token's row of G is zero
     u32x4* p = reinterpret_cast<u32x4*>(Z + (int64_t)r * a.ldz + c0);

@@ -211,3 +211,19 @@ def test_full_size_zero_weight_closed_form():
     untargeted[d["t"]] = False
     assert rel_fro(got["dW"][untargeted], expect[untargeted]) <= 2e-2
     got["handle"].close()
+
+
+@pytest.mark.parametrize("variant", [0, 1], ids=["chunked", "fused"])
+@pytest.mark.parametrize("scale", [25.0, 100.0])
+def test_large_logits(variant, scale):
+    """W scaled so that |z| reaches ~40 / ~160 (a peaked softmax).  The chunked variant's bf16
+    buffer holds z minus the row's 256-column tile maximum, so its accuracy does not depend on the
+    logit scale (rounding z itself would put the gradients 3% / 13% off at these scales); the
+    fused variant forms G from the fp32 accumulators."""
+    from flce_inputs import bf16_bits_from_f32
+    d = make_inputs(512, 256, 4096, "bf16", seed=211)
+    d["W"] = bf16_bits_from_f32((oracle.widen(d["W"], "bf16") * scale).astype(np.float32))
+    want = oracle_full(d)
+    got = run_flce(d, chunk=256, variant=variant)
+    got["handle"].close()
+    compare(got, want, d["t"], 4096, 2e-2, 1e-4, f"scale {scale}, variant {variant}")
