@@ -247,17 +247,25 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
+  // Work items are (row group, vocabulary tile): kRows rows x 256 columns, one 16-byte chunk per
+  // thread, so a block reads its rows' tile maxima as one short contiguous run and each row's
+  // chunks as one contiguous 512-byte (bf16) or 1 KiB (fp32) span.  Tiles vary fastest.
   constexpr int E = Elem<T>::E;
-  const int64_t per_row = a.ldz / E;
-  const int64_t total = per_row * a.rows;
+  constexpr int kChunks = kTile / E;          // chunks per row of a tile
+  constexpr int kRows = 256 / kChunks;        // rows per work item
+  const int tiles = (int)(a.ldz / kTile);
+  const int64_t items = (int64_t)((a.rows + kRows - 1) / kRows) * tiles;
   T* Z = static_cast<T*>(a.z);
   const float scale = a.scale->grad;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(idx / per_row);
-    const int c0 = (int)(idx - (int64_t)r * per_row) * E;
-    // the buffer holds z - M (M: the row's maximum over the 256-column tile, its LSE partial)
-    const float l = a.lse[r] - a.pm[(int64_t)(c0 / kTile) * a.pstride + r];
+  const int tr = threadIdx.x / kChunks;
+  const int tc = threadIdx.x % kChunks;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int tile = (int)(it % tiles);
+    const int r = (int)(it / tiles) * kRows + tr;
+    if (r >= a.rows) continue;
+    const int c0 = tile * kTile + tc * E;
+    // the buffer holds z - M (M: the row's maximum over the tile, its LSE partial)
+    const float l = a.lse[r] - a.pm[(int64_t)tile * a.pstride + r];
     const int64_t tv = a.t[r];
     const bool counted = !a.ign.skip(tv);   // an ignored token's row of G is zero
     u32x4* p = reinterpret_cast<u32x4*>(Z + (int64_t)r * a.ldz + c0);
@@ -515,7 +523,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
 
 hipError_t launch_dlogits(In in, const DlogitsArgs& a, hipStream_t s) {
   const int E = in == In::BF16 ? 8 : 4;
-  const int grid = grid_elementwise(a.ldz / E * a.rows, 256);
+  const int grid = grid_elementwise(a.ldz / E * a.rows, 256);   // one 16-byte chunk per thread
   if (in == In::BF16) hipLaunchKernelGGL(dlogits_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(dlogits_kernel<float>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
