@@ -38,16 +38,19 @@ __device__ __forceinline__ u32x4 g_frag_k(const char* g, int mnb, int ks, int la
   return *reinterpret_cast<const u32x4*>(g + g_off(row, c));
 }
 
-// dW rows operand: vocabulary mnb + l % 32, k = token 16 ks + 8 (l / 32) .. +7
+// dW rows operand: vocabulary mnb + l % 32, k = token 16 ks + 8 (l / 32) .. +7.  Issued as inline
+// asm (the transposing-read builtin makes the compiler wait for every copy in flight first);
+// gemm_stream waits for these reads before its MFMAs.
 __device__ __forceinline__ u32x4 g_frag_t(const char* g, int mnb, int ks, int lane) {
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const int r = 16 * ks + 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int v = mnb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int byte = (v & 7) * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(g + g_off(r, v >> 3) + byte));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(g + g_off(r + 4, v >> 3) + byte));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  const uint32_t a0 = (uint32_t)(uintptr_t)(const lds_i16x4*)(g + g_off(r, v >> 3) + byte);
+  const uint32_t a1 = (uint32_t)(uintptr_t)(const lds_i16x4*)(g + g_off(r + 4, v >> 3) + byte);
+  u32x2 l2, h2;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(l2) : "v"(a0));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h2) : "v"(a1));
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
@@ -85,9 +88,10 @@ __device__ __forceinline__ void gemm_stream(f32x16 (&acc)[kColBlocks][4], char* 
     for (int s = 0; s < 2; ++s) {
       u32x4 a[kColBlocks], b[4];
 #pragma unroll
-      for (int i = 0; i < kColBlocks; ++i) a[i] = read_frag<bf16_t, false>(st, colb + 32 * i, s, lane);
+      for (int i = 0; i < kColBlocks; ++i) a[i] = read_frag<bf16_t, false, true>(st, colb + 32 * i, s, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = rows_frag(rowb + 32 * j, 2 * kt + s, lane);
+      lgkm_wait();   // the transposing reads are asm: the compiler does not wait for them
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
