@@ -4,12 +4,13 @@
 // Cross-Entropy" page, 42jerrykim.github.io):
 //   logits_lse   z = x_c W^T on MFMA; the epilogue reduces each row of the
 //                256-wide vocabulary tile to (max, sum exp(z - max)) in
-//                registers, picks up the target logit, and stores z into the
-//                chunk buffer (online-softmax statistics as on the "Unsloth
-//                deep architecture" page, streaming CE kernel).
+//                registers, picks up the target logit, and stores z - max into
+//                the chunk buffer (online-softmax statistics as on the "Unsloth
+//                deep architecture" page, streaming CE kernel; the shift keeps
+//                the bf16 rounding of the softmax relative at any logit scale).
 //   lse_combine  lse_n = M + ln sum_j s_j e^(m_j - M) over the vocab tiles,
 //                per-row loss lse_n - z[n, t_n] (0 for an ignored token).
-//   dlogits      G = (exp(z - lse) - onehot(t)) * scale written over z
+//   dlogits      G = (exp(z - lse) - onehot(t)) * scale written over z - max
 //                (softmax - one_hot in the same buffer, step 2; scale = 1/N
 //                for the mean over N tokens, the page's reduction).
 //   dx           dx_c (+)= G W (contraction over the vocabulary, split-K).
@@ -243,7 +244,8 @@ __global__ __launch_bounds__(256) void lse_combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// G = (exp(z - lse) - onehot) / N, in place, zero in the padding columns
+// G = (exp(z - lse) - onehot) / N, in place over the buffer of z - M (M: the row's tile
+// maximum), as exp((z - M) - (lse - M)); zero in the padding columns
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
