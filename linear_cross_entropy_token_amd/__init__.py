@@ -211,6 +211,24 @@ def _dt_code(dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
+def _check_tensors(handle_device: int, specs):
+    """Raises ValueError unless every given tensor is a contiguous tensor on the handle's device
+    with the expected shape and dtype.  The C ABI takes plain pointers and cannot see either, so
+    an output of the wrong size or dtype would otherwise be written past its end.
+    specs: (name, tensor or None, shape, dtype); None tensors are skipped."""
+    for name, ten, shape, dtype in specs:
+        if ten is None:
+            continue
+        if not ten.is_cuda or ten.device.index != handle_device:
+            raise ValueError(f"{name} must be on cuda:{handle_device}, not {ten.device}")
+        if tuple(ten.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(ten.shape)}, expected {tuple(shape)}")
+        if ten.dtype != dtype:
+            raise ValueError(f"{name} has dtype {ten.dtype}, expected {dtype}")
+        if not ten.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 class FusedLinearCrossEntropy:
     """Owns one library handle; takes torch device tensors.
 
@@ -286,11 +304,12 @@ class FusedLinearCrossEntropy:
             lse = torch.empty((N,), dtype=torch.float32, device=x.device) if with_lse else None
         else:
             loss, dx, dW, lse = out
-        for name, ten in (("x", x), ("W", W), ("targets", t), ("dx", dx), ("dW", dW)):
-            if not ten.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-        if x.dtype != self.in_dtype or W.dtype != self.in_dtype or t.dtype != torch.int64:
-            raise ValueError("dtype mismatch with the handle's configuration")
+        if dx is None or dW is None:
+            raise ValueError("forward_backward needs dx and dW outputs (forward() computes the loss only)")
+        _check_tensors(self.device, (("x", x, (N, H), self.in_dtype), ("W", W, (V, H), self.in_dtype),
+                                     ("targets", t, (N,), torch.int64), ("loss", loss, (), torch.float32),
+                                     ("dx", dx, (N, H), self.dx_dtype), ("dW", dW, (V, H), self.dw_dtype),
+                                     ("lse", lse, (N,), torch.float32)))
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
         opt = _options(reduction, ignore_index, FLCE_ACCUMULATE if accumulate else 0)
         st = flce_forward_backward_opt(self.handle, x.data_ptr(), W.data_ptr(), t.data_ptr(), N, H, V,
@@ -306,11 +325,8 @@ class FusedLinearCrossEntropy:
         import torch
         N, H = x.shape
         V = W.shape[0]
-        for name, ten in (("x", x), ("W", W), ("targets", t)):
-            if not ten.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-        if x.dtype != self.in_dtype or W.dtype != self.in_dtype or t.dtype != torch.int64:
-            raise ValueError("dtype mismatch with the handle's configuration")
+        _check_tensors(self.device, (("x", x, (N, H), self.in_dtype), ("W", W, (V, H), self.in_dtype),
+                                     ("targets", t, (N,), torch.int64)))
         loss = torch.empty((), dtype=torch.float32, device=x.device)
         lse = torch.empty((N,), dtype=torch.float32, device=x.device) if with_lse else None
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
@@ -339,13 +355,13 @@ def _rmsnorm_call(self, hidden, gamma, W, t, eps, chunk, with_lse, out, stream, 
         lse = torch.empty((N,), dtype=torch.float32, device=hidden.device) if with_lse else None
     else:
         loss, dh, dg, dW, lse = out
-    for name, ten in (("hidden", hidden), ("gamma", gamma), ("W", W), ("targets", t), ("dhidden", dh),
-                      ("dgamma", dg), ("dW", dW)):
-        if ten is not None and not ten.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if hidden.dtype != self.in_dtype or gamma.dtype != self.in_dtype or W.dtype != self.in_dtype \
-            or t.dtype != torch.int64:
-        raise ValueError("dtype mismatch with the handle's configuration")
+    if grads and (dh is None or dg is None or dW is None):
+        raise ValueError("the backward needs dhidden, dgamma and dW outputs")
+    _check_tensors(self.device, (("hidden", hidden, (N, H), self.in_dtype), ("gamma", gamma, (H,), self.in_dtype),
+                                 ("W", W, (V, H), self.in_dtype), ("targets", t, (N,), torch.int64),
+                                 ("loss", loss, (), torch.float32), ("dhidden", dh, (N, H), self.dx_dtype),
+                                 ("dgamma", dg, (H,), self.dw_dtype), ("dW", dW, (V, H), self.dw_dtype),
+                                 ("lse", lse, (N,), torch.float32)))
     s = stream if stream is not None else torch.cuda.current_stream(hidden.device)
     ptr = (lambda ten: ten.data_ptr() if ten is not None else None)
     st = flce_rmsnorm_forward_backward(self.handle, hidden.data_ptr(), gamma.data_ptr(), eps, W.data_ptr(),

@@ -74,3 +74,12 @@ def test_null_handle_is_rejected():
     assert flce.flce_workspace_bytes(None, 10, 8, 10, 0) == 0
     assert flce.flce_forward_backward(None, 1, 1, 1, 1, 8, 1, 0, 1, 1, 1, None) == 1
     assert flce.flce_destroy(None) == 0
+
+
+def test_wrapper_tensor_checks_on_cpu():
+    """The wrapper's checks run before any library call: a CPU tensor is refused, None is skipped."""
+    torch = pytest.importorskip("torch")
+    from linear_cross_entropy_token_amd import _check_tensors
+    _check_tensors(0, (("lse", None, (4,), torch.float32),))
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        _check_tensors(0, (("x", torch.zeros(2, 3), (2, 3), torch.float32),))
