@@ -25,6 +25,9 @@
  *    no use of the null stream by the library itself (the stream/event
  *    ordering rules of the async continuous-batching page, pogovet.com).
  *    Results are valid once the stream reaches that point.
+ *  - No output may overlap an input or another output (byte ranges are
+ *    compared; INVALID_ARG otherwise): later chunks read x and W after
+ *    earlier chunks have written dx and dW.
  *  - Validation happens before any launch; a call that returns an error
  *    writes nothing.  Nothing aborts and no exception crosses the ABI.
  *  - A handle must not be used by two calls at the same time.
@@ -89,8 +92,8 @@ flce_status_t flce_destroy(flce_handle_t h);
  *                  and a device flag is raised that flce_check reports as FLCE_ERR_DATA.
  *   chunk          tokens per chunk; <= 0 selects the automatic size (flce_effective_chunk)
  *   loss    [1]    fp32, overwritten with the mean loss over the N tokens
- *   dx      [N,H]  cfg.dx_dtype, overwritten (must not alias x)
- *   dW      [V,H]  cfg.dw_dtype, overwritten (must not alias W)
+ *   dx      [N,H]  cfg.dx_dtype, overwritten
+ *   dW      [V,H]  cfg.dw_dtype, overwritten
  * The workspace grows on demand (hipMalloc/hipFree, which synchronise the device); call
  * flce_reserve beforehand to keep allocation out of timed or captured regions.
  * Errors: INVALID_ARG, UNSUPPORTED, OOM (outputs untouched), HIP. */
@@ -158,7 +161,7 @@ size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V
  *   dW      [V,H]  cfg.dw_dtype                    eps >= 0 (finite)
  * Options as for flce_forward_backward_opt (accumulate adds into dhidden, dgamma and dW;
  * forward only needs none of them).  Chunked variant only; H <= 32768.
- * Errors: INVALID_ARG (NULL pointers, bad options, eps < 0 or NaN, aliasing outputs),
+ * Errors: INVALID_ARG (NULL pointers, bad options, eps < 0 or NaN, overlapping tensors),
  * UNSUPPORTED (fused variant, H > 32768, alignment, size limits), OOM, HIP. */
 flce_status_t flce_rmsnorm_forward_backward(flce_handle_t h, const void* hidden, const void* gamma, float eps,
                                             const void* W, const int64_t* targets, int64_t N, int64_t H,

@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -233,6 +234,30 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte range [lo, hi) of one caller tensor; empty for a null pointer.
+struct Span {
+  uintptr_t lo = 0, hi = 0;
+  Span(const void* p, int64_t bytes) {
+    if (p != nullptr && bytes > 0) {
+      lo = reinterpret_cast<uintptr_t>(p);
+      hi = lo + (uintptr_t)bytes;
+    }
+  }
+};
+inline bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// True when no output overlaps an input or another output: the kernels read inputs after
+// outputs have been written (later chunks read x and W after earlier chunks wrote dx and dW).
+bool outputs_disjoint(std::initializer_list<Span> in, std::initializer_list<Span> out) {
+  for (auto o = out.begin(); o != out.end(); ++o) {
+    for (const Span& i : in)
+      if (overlap(*o, i)) return false;
+    for (auto o2 = o + 1; o2 != out.end(); ++o2)
+      if (overlap(*o, *o2)) return false;
+  }
+  return true;
+}
 
 flce_status_t ensure_workspace(flce_handle_s* h, size_t need) {
   if (h->cfg.workspace_limit > 0 && need > (size_t)h->cfg.workspace_limit) return FLCE_ERR_OOM;
@@ -737,7 +762,14 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
       (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return FLCE_ERR_UNSUPPORTED;
-  if (o.grads && (dx == x || dW == W)) return FLCE_ERR_INVALID_ARG;
+  {
+    const int64_t es = (int64_t)in_size(h->cfg);
+    const int64_t dx_es = h->cfg.dx_dtype == FLCE_BF16 ? 2 : 4, dw_es = h->cfg.dw_dtype == FLCE_BF16 ? 2 : 4;
+    if (!outputs_disjoint({Span(x, N * H * es), Span(W, V * H * es), Span(targets, N * 8)},
+                          {Span(loss, 4), Span(o.grads ? dx : nullptr, N * H * dx_es),
+                           Span(o.grads ? dW : nullptr, V * H * dw_es), Span(lse, N * 4)}))
+      return FLCE_ERR_INVALID_ARG;
+  }
   const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads);
   const flce_status_t ws = ensure_workspace(h, p.total);
   if (ws != FLCE_OK) return ws;
@@ -776,7 +808,15 @@ flce_status_t flce_rmsnorm_forward_backward(flce_handle_t h, const void* hidden,
       (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u) ||
       (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return FLCE_ERR_UNSUPPORTED;
-  if (o.grads && (dhidden == hidden || dW == W || dgamma == gamma)) return FLCE_ERR_INVALID_ARG;
+  {
+    const int64_t es = (int64_t)in_size(h->cfg);
+    const int64_t dx_es = h->cfg.dx_dtype == FLCE_BF16 ? 2 : 4, dw_es = h->cfg.dw_dtype == FLCE_BF16 ? 2 : 4;
+    if (!outputs_disjoint({Span(hidden, N * H * es), Span(gamma, H * es), Span(W, V * H * es), Span(targets, N * 8)},
+                          {Span(loss, 4), Span(o.grads ? dhidden : nullptr, N * H * dx_es),
+                           Span(o.grads ? dgamma : nullptr, H * dw_es), Span(o.grads ? dW : nullptr, V * H * dw_es),
+                           Span(lse, N * 4)}))
+      return FLCE_ERR_INVALID_ARG;
+  }
   const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads, true);
   const flce_status_t ws = ensure_workspace(h, p.total);
   if (ws != FLCE_OK) return ws;
