@@ -35,8 +35,25 @@ def _run(cmd):
     return out
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c", "flce_c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c", "flce_c_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_client() -> str:
+    """Compiles the plain-C test client of the ABI (C99, gcc) against LIB and the HIP runtime."""
+    tmp = C_CLIENT + ".tmp"
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"), C_CLIENT_SRC,
+          "-L", PKG, "-lflce", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+          "-Wl,-rpath,$ORIGIN/../../linear_cross_entropy_token_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+          "-o", tmp])
+    os.replace(tmp, C_CLIENT)
+    return C_CLIENT
+
+
 def build(verbose: bool = False) -> str:
-    """Compiles every source and links LIB.  Always recompiles."""
+    """Compiles every source and links LIB, then the C test client.  Always recompiles."""
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
     cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
@@ -45,6 +62,8 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     outs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, LIB)
+    if os.path.exists(C_CLIENT_SRC):
+        build_c_client()
     if verbose:
         for o in outs:
             if o.strip():
