@@ -148,6 +148,31 @@ def materialised_peak(x, W, t):
         return {"extra_gb": None, "status": "OOM"}
 
 
+def hipblaslt_yardstick(x, W, rows: int, reps: int = 10):
+    """torch.matmul (hipBLASLt) on one chunk's three products in the layouts the library uses:
+    logits x_c W^T, dx G W and dW G^T x_c, with a random G of the chunk's shape; ms and TFLOP/s
+    per product, 2 rows V H flops each (a reference point, not part of the step)."""
+    import torch
+    xc = x[:rows]
+    g = torch.randn(rows, W.shape[0], device=x.device, dtype=x.dtype)
+    fl = 2.0 * rows * W.shape[0] * W.shape[1]
+    res = {}
+    for name, fn in (("logits_lse", lambda: xc @ W.T), ("dx", lambda: g @ W), ("dw", lambda: g.T @ xc)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"avg_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+    del g
+    torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +198,8 @@ def main():
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="after the run, copy a buffer of this many GiB once (a plain copy kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the chunk's three products")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -324,6 +351,11 @@ def main():
         extra["copy_calibration_bytes"] = n * 4
         del src, dst
 
+    yard = None
+    if args.yardstick:
+        log("[bench] timing torch.matmul on the chunk's three products")
+        yard = hipblaslt_yardstick(x, W, eff_chunk)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
@@ -347,6 +379,8 @@ def main():
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
     }
+    if yard is not None:
+        rec["yardstick_hipblaslt"] = yard
     print(json.dumps(rec), flush=True)
 
 
