@@ -39,7 +39,8 @@ from typing import Dict, Iterable
 import numpy as np
 
 __all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce",
-           "flce_rows", "flce_ext", "rmsnorm", "rmsnorm_backward", "rmsnorm_flce", "logits_bytes"]
+           "flce_rows", "flce_sparse_weight", "flce_ext", "rmsnorm", "rmsnorm_backward", "rmsnorm_flce",
+           "logits_bytes"]
 
 
 def widen(arr: np.ndarray, dtype: str) -> np.ndarray:
@@ -230,6 +231,51 @@ def flce_rows(x: np.ndarray, W: np.ndarray, t: np.ndarray, rows: Iterable[int],
     G = dlogits(Z, ts, lse, n_total)
     del Z
     return {"lse": lse, "loss": loss, "dx": G @ W}
+
+
+def flce_sparse_weight(x: np.ndarray, W_nz: np.ndarray, nz: np.ndarray, V: int, t: np.ndarray,
+                       dw_rows: Iterable[int]) -> Dict[str, np.ndarray]:
+    """``flce`` for a [V,H] weight that is zero outside the rows ``nz``, without forming it.
+
+    The same definition, evaluated where the zero rows make it explicit: a zero row's logit is 0
+    for every token, so lse_n = ln(sum_{r in nz} e^{z[n,r]} + (V - |nz|) e^0) with z = x W_nz^T;
+    a zero row adds nothing to dx = G W; and a zero row v has G[n,v] = (e^{-lse_n} - [t_n = v]) / N,
+    so dW[v] = sum_n G[n,v] x_n needs no logits of its own.  Returns the loss (mean over N), lse
+    [N], dx [N,H], and dW for the rows ``dw_rows`` (in that order).  For checking weights too
+    large for ``flce`` to hold in host memory; pinned against ``flce`` on small dense cases.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W_nz = np.asarray(W_nz, dtype=np.float64)
+    nz = np.asarray(nz, dtype=np.int64)
+    t = np.asarray(t, dtype=np.int64)
+    if np.any(np.diff(nz) <= 0) or (len(nz) and (nz[0] < 0 or nz[-1] >= V)):
+        raise ValueError("nz must be increasing ids in [0, V)")
+    if t.min() < 0 or t.max() >= V:
+        raise ValueError("targets out of range")
+    N, k = x.shape[0], len(nz)
+    n_zero = V - k
+    Zs = logits(x, W_nz)                                           # [N, k]
+    m = Zs.max(axis=1) if k else np.full(N, -np.inf)
+    if n_zero > 0:
+        m = np.maximum(m, 0.0)
+    lse = m + np.log(np.exp(Zs - m[:, None]).sum(axis=1) + n_zero * np.exp(-m))
+    j_t = np.searchsorted(nz, t)
+    hit = (j_t < k) & (nz[np.minimum(j_t, max(k - 1, 0))] == t) if k else np.zeros(N, dtype=bool)
+    z_t = np.where(hit, Zs[np.arange(N), np.minimum(j_t, max(k - 1, 0))] if k else 0.0, 0.0)
+    loss = float((lse - z_t).mean())
+    Gs = np.exp(Zs - lse[:, None])
+    Gs[np.arange(N)[hit], j_t[hit]] -= 1.0
+    Gs /= N
+    dx = Gs @ W_nz
+    base = (np.exp(-lse) / N) @ x                                  # sum_n e^{-lse_n} x_n / N
+    out = []
+    for v in dw_rows:
+        j = int(np.searchsorted(nz, v))
+        if j < k and nz[j] == v:
+            out.append(Gs[:, j] @ x)
+        else:
+            out.append(base - x[t == v].sum(axis=0) / N)
+    return {"loss": loss, "lse": lse, "dx": dx, "dW_rows": np.array(out).reshape(len(out), x.shape[1])}
 
 
 def logits_bytes(n_tokens: int, vocab: int, bytes_per_elem: int) -> int:

@@ -213,6 +213,40 @@ def test_rows_match_full():
     np.testing.assert_allclose(rr["dx"], r["dx"][rows], rtol=1e-11, atol=1e-17)
 
 
+@pytest.mark.parametrize("case", ["mixed", "targets_only_in_zero_rows", "targets_only_in_nonzero_rows",
+                                  "no_zero_rows", "all_zero"])
+def test_sparse_weight_matches_dense(case):
+    """flce_sparse_weight against flce on the dense weight it stands for (zero outside nz)."""
+    rng = np.random.default_rng(17)
+    N, H, V = 48, 24, 300
+    x = rng.standard_normal((N, H))
+    if case == "no_zero_rows":
+        nz = np.arange(V)
+    elif case == "all_zero":
+        nz = np.array([], dtype=np.int64)
+    else:
+        nz = np.unique(np.concatenate([rng.choice(V, 40, replace=False), [V - 1, V - 2]]))
+    W_nz = rng.standard_normal((len(nz), H)) * 0.7      # large enough logits to matter
+    zero = np.setdiff1d(np.arange(V), nz)
+    if case == "targets_only_in_zero_rows":
+        t = rng.choice(zero, N)
+    elif case == "targets_only_in_nonzero_rows":
+        t = rng.choice(nz, N)
+    else:
+        t = rng.integers(0, V, N)
+    W = np.zeros((V, H))
+    W[nz] = W_nz
+    want = oracle.flce(x, W, t)
+    rows = np.unique(np.concatenate([t[:5], zero[:3], nz[:3], [V - 1]]))
+    got = oracle.flce_sparse_weight(x, W_nz, nz, V, t, rows)
+    np.testing.assert_allclose(got["loss"], want["loss"], rtol=1e-13)
+    np.testing.assert_allclose(got["lse"], want["lse"], rtol=1e-13)
+    np.testing.assert_allclose(got["dx"], want["dx"], rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(got["dW_rows"], want["dW"][rows], rtol=1e-10, atol=1e-15)
+    if case == "all_zero":                                 # the W = 0 closed form
+        assert abs(got["loss"] - np.log(V)) <= 1e-14 * np.log(V)
+
+
 def test_statistical_expectation_of_loss():
     """x ~ N(0,1), W ~ N(0,0.02^2): logits ~ N(0, 4e-4 |x|^2), so E[loss] ~ ln V + 2e-4 H."""
     w = WORKLOADS["tiny_fp32"]
