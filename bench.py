@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "FLCE fwd+bwd tokens/s (V=128256,H=4096,bf16); % MFMA peak; peak HBM"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}      # MI355X published dense MFMA peaks
+PEAK_SCLK_MHZ = 2400.0                               # the engine clock those peaks assume
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -317,6 +318,8 @@ def main():
              "share": round(s["total_ms"] / args.steps / ms, 4)}
         if s["flops"] > 0:
             k["tflops"] = round(s["flops"] / s["launches"] / (avg * 1e-3) / 1e12, 1)
+            if s.get("sclk_mhz"):
+                k["sclk_mhz"] = round(s["sclk_mhz"], 1)
         elif s["bytes"] > 0:
             k["gbs"] = round(s["bytes"] / s["launches"] / (avg * 1e-3) / 1e9, 1)
         kernels[name] = k
@@ -330,6 +333,11 @@ def main():
                 "traffic": measured_traffic(dom, w.name, eff_chunk),
                 "flops_per_launch": ds["flops"] / ds["launches"],
                 "avg_launch_ms": round(avg_s * 1e3, 4)}
+    if ds.get("sclk_mhz"):
+        # the same peak scaled to the shader clock the kernel's workgroups ran at (s_memtime
+        # against the 100 MHz real-time counter, summed over its workgroups)
+        roofline["observed_sclk_mhz"] = round(ds["sclk_mhz"], 1)
+        roofline["frac_at_observed_sclk"] = round(achieved / (peak_tf * ds["sclk_mhz"] / PEAK_SCLK_MHZ), 4)
 
     extra = {"peak_extra_gb": round(peak_extra / 1e9, 3), "peak_extra_gib": round(peak_extra / 2**30, 3),
              "dx_dtype": str(gdt).replace("torch.", ""), "dw_dtype": str(gdt).replace("torch.", ""),

@@ -193,16 +193,20 @@ flce_status_t flce_check(flce_handle_t h, void* stream);
 /* ---- per-kernel timing (tracing) ----------------------------------------------------
  * When enabled, every launch a call makes is bracketed by HIP events recorded on the
  * caller's stream, so each kernel's duration is the time between the event before it and
- * the event after it on that stream.  Enabling (or disabling) resets the statistics. */
+ * the event after it on that stream.  The GEMM kernels (logits_lse, dx, dw) also time each of
+ * their workgroups with the shader-clock counter and the 100 MHz real-time counter, whose ratio
+ * is the shader clock the GEMMs actually ran at.  Enabling (or disabling) resets the statistics;
+ * enabling allocates 2 * 8 bytes of device memory per kernel kind once per handle. */
 typedef struct {
   char name[32];          /* kernel name, e.g. "logits_lse", "dx", "dw" */
   int64_t launches;       /* launches timed since the last reset */
   double total_ms;        /* summed durations of those launches */
   double flops;           /* summed algorithmic flops: 2*rows*V*H for each GEMM launch, 0 otherwise */
   double bytes;           /* summed algorithmic HBM bytes (each operand read once, each result written once) */
+  double sclk_mhz;        /* GEMM kernels: mean shader clock over their workgroups' lifetimes, MHz (0: not timed) */
 } flce_kernel_stat_t;
 
-/* Errors: INVALID_ARG (null handle). */
+/* Errors: INVALID_ARG (null handle), OOM, HIP. */
 flce_status_t flce_profile_enable(flce_handle_t h, int enable);
 
 /* Synchronises on the recorded events, folds them into the statistics and copies up to

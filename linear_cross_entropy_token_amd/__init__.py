@@ -53,7 +53,7 @@ class Options(ctypes.Structure):
 
 class KernelStat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
-                ("flops", ctypes.c_double), ("bytes", ctypes.c_double)]
+                ("flops", ctypes.c_double), ("bytes", ctypes.c_double), ("sclk_mhz", ctypes.c_double)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -188,7 +188,7 @@ def flce_profile_enable(handle, enable) -> int:
 
 
 def flce_profile_read(handle):
-    """Returns (status, {kernel name: dict(launches, total_ms, flops, bytes)})."""
+    """Returns (status, {kernel name: dict(launches, total_ms, flops, bytes, sclk_mhz)})."""
     arr = (KernelStat * 16)()
     n = ctypes.c_int()
     st = load_library().flce_profile_read(handle, arr, 16, ctypes.byref(n))
@@ -196,7 +196,7 @@ def flce_profile_read(handle):
     for i in range(min(n.value, 16)):
         k = arr[i]
         out[k.name.decode()] = {"launches": k.launches, "total_ms": k.total_ms, "flops": k.flops,
-                                "bytes": k.bytes}
+                                "bytes": k.bytes, "sclk_mhz": k.sclk_mhz}
     return st, out
 
 

@@ -85,6 +85,7 @@ struct flce_handle_s {
   size_t ws_bytes = 0;
   int* flag = nullptr;      // device int, bit 0 = out-of-range target seen
   bool profiling = false;
+  unsigned long long* clk = nullptr;   // device [K_COUNT][2]: GEMM workgroup lifetimes (shader, 100 MHz ticks)
   std::vector<Mark> marks;  // pending events, in stream order
   std::vector<hipEvent_t> pool;
   Stat stats[K_COUNT];
@@ -107,6 +108,11 @@ struct DeviceGuard {
     if (changed) (void)hipSetDevice(prev);
   }
 };
+
+// The device clock counters of a GEMM kernel kind while profiling, else null.
+unsigned long long* clock_of(flce_handle_s* h, int kind) {
+  return h->profiling && h->clk != nullptr ? h->clk + 2 * kind : nullptr;
+}
 
 // Records a profiling event before a launch of `kind` (or kind -1 after the last launch).
 hipError_t mark(flce_handle_s* h, int kind, double flops, double bytes, hipStream_t st) {
@@ -364,6 +370,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   la.V = (int)p.V;
   la.tiles_m = tiles_m;
   la.tiles_n = p.tiles_v;
+  la.clk = clock_of(h, K_LOGITS);
   FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
   FLCE_LAUNCH(flce::launch_logits(in, la, st));
 
@@ -414,6 +421,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   xa.tiles_n = p.tiles_h;
   xa.dx_fp32 = dxo.fp32;
   xa.accumulate = dxo.accumulate;
+  xa.clk = clock_of(h, K_DX);
   FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
   FLCE_LAUNCH(flce::launch_dx(in, xa, st));
   if (p.splits > 1) {
@@ -441,6 +449,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   wa.tiles_n = p.tiles_h;
   wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
   wa.accumulate = s > 0 || o.accumulate;
+  wa.clk = clock_of(h, K_DW);
   FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
                    zbytes + (double)rows * p.H * b_in + VH * b_dw * (wa.accumulate ? 2.0 : 1.0), st));
   FLCE_LAUNCH(flce::launch_dw(in, wa, st));
@@ -581,6 +590,7 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
     la.V = (int)p.V;
     la.tiles_m = tiles_m;
     la.tiles_n = p.tiles_v;
+    la.clk = clock_of(h, K_LOGITS);
     FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * 2 + VH * 2, st));
     FLCE_LAUNCH(flce::launch_logits(In::BF16, la, st));
 
@@ -718,6 +728,7 @@ flce_status_t flce_destroy(flce_handle_t h) {
     for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
     if (h->ws != nullptr) (void)hipFree(h->ws);
     if (h->flag != nullptr) (void)hipFree(h->flag);
+    if (h->clk != nullptr) (void)hipFree(h->clk);
   }
   delete h;
   return FLCE_OK;
@@ -845,6 +856,16 @@ flce_status_t flce_profile_enable(flce_handle_t h, int enable) {
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
   (void)fold_marks(h);
   for (Stat& s : h->stats) s = Stat{};
+  if (enable != 0) {
+    const size_t bytes = 2 * K_COUNT * sizeof(unsigned long long);
+    if (h->clk == nullptr && hipMalloc(reinterpret_cast<void**>(&h->clk), bytes) != hipSuccess) {
+      h->clk = nullptr;
+      (void)hipGetLastError();
+      return FLCE_ERR_OOM;
+    }
+    const std::vector<unsigned long long> zero(2 * K_COUNT, 0ull);
+    if (hipMemcpy(h->clk, zero.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) return FLCE_ERR_HIP;
+  }
   h->profiling = enable != 0;
   return FLCE_OK;
 }
@@ -854,7 +875,12 @@ flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int ca
     return FLCE_ERR_INVALID_ARG;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
-  const hipError_t e = fold_marks(h);
+  hipError_t e = fold_marks(h);
+  unsigned long long clk[2 * K_COUNT] = {};
+  if (h->clk != nullptr) {
+    const hipError_t e2 = hipMemcpy(clk, h->clk, sizeof(clk), hipMemcpyDeviceToHost);
+    if (e2 != hipSuccess) e = e2;
+  }
   int n = 0;
   for (int k = 0; k < K_COUNT; ++k) {
     const Stat& s = h->stats[k];
@@ -867,6 +893,7 @@ flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int ca
       o.total_ms = s.ms;
       o.flops = s.flops;
       o.bytes = s.bytes;
+      o.sclk_mhz = clk[2 * k + 1] > 0 ? 100.0 * (double)clk[2 * k] / (double)clk[2 * k + 1] : 0.0;
     }
     ++n;
   }

@@ -539,4 +539,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
 
+// Adds the workgroup's lifetime, from construction to the end of its scope, to clk[0] in
+// shader-clock ticks (s_memtime) and to clk[1] in 100 MHz real-time ticks (s_memrealtime) when clk
+// is set: summed over the workgroups of a launch, their ratio is the shader clock it ran at.
+struct ClockSpan {
+  unsigned long long* clk;
+  uint64_t t0, r0;
+  __device__ explicit ClockSpan(unsigned long long* c) : clk(c), t0(0), r0(0) {
+    if (clk != nullptr) {
+      t0 = __builtin_amdgcn_s_memtime();
+      r0 = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ ~ClockSpan() {
+    if (clk != nullptr && threadIdx.x == 0) {
+      const uint64_t t1 = __builtin_amdgcn_s_memtime();
+      const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+      atomicAdd(clk, (unsigned long long)(t1 - t0));
+      atomicAdd(clk + 1, (unsigned long long)(r1 - r0));
+    }
+  }
+};
+
 }  // namespace flce

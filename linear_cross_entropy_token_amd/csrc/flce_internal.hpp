@@ -49,6 +49,7 @@ struct LogitsArgs {
   int pstride;
   int rows, H, V;
   int tiles_m, tiles_n;
+  unsigned long long* clk; // null, or [2]: summed workgroup lifetimes in shader-clock and 100 MHz ticks
 };
 
 struct CombineArgs {
@@ -87,6 +88,7 @@ struct DxArgs {
   int tiles_m, tiles_n;
   int dx_fp32;
   int accumulate;       // 0: overwrite dx rows, 1: dx += G W (splits == 1 only; else in the reduce)
+  unsigned long long* clk; // null, or [2]: summed workgroup lifetimes in shader-clock and 100 MHz ticks
 };
 
 struct DxReduceArgs {
@@ -108,6 +110,7 @@ struct DwArgs {
   int tiles_m, tiles_n;
   int dw_fp32;
   int accumulate;       // 0: overwrite dW, 1: dW += G^T x
+  unsigned long long* clk; // null, or [2]: summed workgroup lifetimes in shader-clock and 100 MHz ticks
 };
 
 struct FinalizeArgs {

@@ -30,6 +30,7 @@ static_assert(kTile == kTileM && kTile == kTileN, "tile sizes of the dispatcher 
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
+  const ClockSpan span(a.clk);
   constexpr int kEpiBytes = 2 * kWaveCols * kTile * (int)sizeof(float) + kTile * (int)sizeof(int);
   static_assert(kSmemBytes + kEpiBytes <= kDeepRingBytes, "epilogue scratch fits behind the z tile");
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
@@ -293,6 +294,7 @@ __global__ __launch_bounds__(256) void dlogits_kernel(DlogitsArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
+  const ClockSpan span(a.clk);
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const int tiles = a.tiles_m * a.tiles_n;
   const int L = xcd_remap(blockIdx.x, tiles * a.splits);
@@ -373,6 +375,7 @@ __global__ __launch_bounds__(256) void dx_reduce_kernel(DxReduceArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
+  const ClockSpan span(a.clk);
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int tid = threadIdx.x;
   const int L = xcd_remap(blockIdx.x, a.tiles_m * a.tiles_n);
