@@ -34,11 +34,11 @@ finite differences and a hand-derived worked example (tests/golden).
 """
 from __future__ import annotations
 
-from typing import Dict, Iterable
+from typing import Callable, Dict, Iterable, Optional
 
 import numpy as np
 
-__all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce",
+__all__ = ["widen", "logits", "row_logsumexp", "row_losses", "dlogits", "flce", "flce_blocked",
            "flce_rows", "flce_sparse_weight", "flce_ext", "rmsnorm", "rmsnorm_backward", "rmsnorm_flce",
            "logits_bytes"]
 
@@ -115,6 +115,63 @@ def flce(x: np.ndarray, W: np.ndarray, t: np.ndarray) -> Dict[str, np.ndarray]:
     dx = G @ W
     dW = G.T @ x
     return {"loss": float(losses.mean()), "dx": dx, "dW": dW, "lse": lse, "losses": losses}
+
+
+def flce_blocked(x: np.ndarray, W: np.ndarray, t: np.ndarray, block: int, dtype: str = "fp64",
+                 dx_blocks: Optional[Iterable[int]] = None,
+                 progress: Optional[Callable[[int, int], None]] = None) -> Dict[str, np.ndarray]:
+    """``flce`` computed one block of ``block`` token rows at a time.
+
+    This is the token-chunk loop of the FLCE page's core idea, in fp64 and
+    with the plain functions above: for the rows [s, e) of a block, the
+    logits Z_b = x_b W^T, their log-sum-exp and losses, the block's rows of
+    G (scaled by 1/N for the GLOBAL token count N, as the page divides by
+    the whole batch's token count), the block's rows of dx = G_b W, and the
+    block's term G_b^T x_b of dW, which is summed over the blocks.  Every
+    quantity is the same as ``flce``'s up to the order of the dW sum; only
+    one block's logits exist at a time, so problems whose [N,V] logits do
+    not fit in host memory can be checked whole.
+
+    ``x`` and ``W`` may be in storage form (``dtype`` "bf16" bit patterns,
+    "fp32"), widened exactly block by block.  ``dx_blocks``: indices of the
+    blocks whose dx rows are formed (default: all); their rows are returned
+    in ``dx`` (stacked in block order) with their row ids in ``dx_rows``.
+    ``progress(b, n_blocks)`` is called after each block.
+    """
+    W = widen(W, dtype)
+    t = np.asarray(t, dtype=np.int64)
+    N, V = x.shape[0], W.shape[0]
+    if N == 0:
+        raise ValueError("N must be positive (the mean over zero tokens is undefined)")
+    if block < 1:
+        raise ValueError("block must be positive")
+    if t.shape != (N,) or t.min() < 0 or t.max() >= V:
+        raise ValueError("targets out of range")
+    n_blocks = (N + block - 1) // block
+    want_dx = set(range(n_blocks)) if dx_blocks is None else set(int(b) for b in dx_blocks)
+    lse = np.empty(N)
+    losses = np.empty(N)
+    dW = np.zeros_like(W)
+    dx_parts, dx_rows = [], []
+    for b in range(n_blocks):
+        s, e = b * block, min(N, (b + 1) * block)
+        xb = widen(x[s:e], dtype)
+        Z = logits(xb, W)
+        lse[s:e] = row_logsumexp(Z)
+        losses[s:e] = row_losses(Z, t[s:e], lse[s:e])
+        G = dlogits(Z, t[s:e], lse[s:e], N)
+        del Z
+        if b in want_dx:
+            dx_parts.append(G @ W)
+            dx_rows.append(np.arange(s, e))
+        dW += G.T @ xb
+        del G
+        if progress is not None:
+            progress(b, n_blocks)
+    H = W.shape[1]
+    return {"loss": float(losses.mean()), "lse": lse, "losses": losses, "dW": dW,
+            "dx": np.concatenate(dx_parts) if dx_parts else np.zeros((0, H)),
+            "dx_rows": np.concatenate(dx_rows) if dx_rows else np.zeros(0, dtype=np.int64)}
 
 
 def flce_ext(x: np.ndarray, W: np.ndarray, t: np.ndarray, reduction: str = "mean",

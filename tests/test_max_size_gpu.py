@@ -70,25 +70,3 @@ def test_largest_weight_under_the_limit():
     assert rel_fro(got["dW"][last], want["dW_rows"][last]) <= 2e-2
     untargeted = ~np.isin(rows, t)                        # pure softmax rows
     assert rel_fro(got["dW"][untargeted], want["dW_rows"][untargeted]) <= 2e-2
-
-
-def test_largest_chunk_buffer():
-    """The Llama-3 vocabulary workload in one chunk of all 16,384 tokens: the logits buffer is
-    16,384 x 128,256 bf16 = 4.20 GB, just under the limit, so its last rows sit at the largest
-    offsets of the dlogits, dx and dW launches.  Sampled rows (the last ones included) of lse and
-    dx against the oracle, and the loss against its expectation for these distributions."""
-    import math
-    from flce_inputs import WORKLOADS
-    from flce_testlib import run_flce
-    require_gpu()
-    w = WORKLOADS["llama3_vocab"]
-    print(f"[max size] {w.name} in one chunk of {w.N} (buffer {w.N * w.V * 2 / 1e9:.2f} GB)", flush=True)
-    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
-    got = run_flce(d, chunk=w.N, with_lse=True)
-    got["handle"].close()
-    rows = [0, 1, w.N // 2, w.N - 3, w.N - 2, w.N - 1]
-    want = oracle.flce_rows(oracle.widen(d["x"][rows], "bf16"), oracle.widen(d["W"], "bf16"), d["t"][rows],
-                            range(len(rows)), w.N)
-    assert np.max(np.abs(got["lse"][rows] - want["lse"])) <= 1e-4 * np.max(np.abs(want["lse"]))
-    assert rel_fro(got["dx"][rows], want["dx"]) <= 2e-2
-    assert abs(got["loss"] - (math.log(w.V) + 2e-4 * w.H)) < 0.1

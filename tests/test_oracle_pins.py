@@ -280,3 +280,108 @@ def test_page_logit_sizes():
             assert fgr["tokens"] * fgr["vocab"] == fgr["elements"], fgr["cite"]
         unit = 1e9 if fgr["unit"] == "GB" else 2.0 ** 30
         assert abs(b / unit - fgr["printed"]) <= fgr["rel_tol"] * fgr["printed"], fgr["cite"]
+
+
+# ---- the row-blocked driver (flce_blocked) ---------------------------------
+# The full-size GPU parity tests compare against flce_blocked, which runs the definition one
+# block of token rows at a time.  It is pinned the way flce is (every check of the pin suite,
+# with blocks that split every pin's tokens, ragged last block included), against flce itself,
+# and by planted mistakes of the kind a blocked loop invites.
+
+def _blocked(block):
+    def f(x, W, t):
+        return oracle.flce_blocked(x, W, t, block=block)
+    return f
+
+
+@pytest.mark.parametrize("block", [1, 2, 3])
+@pytest.mark.parametrize("check", pins.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_blocked_pin(check, block):
+    check(_blocked(block))
+
+
+@pytest.mark.parametrize("N,block", [(1, 1), (7, 3), (64, 64), (64, 100), (65, 16), (200, 7)])
+def test_blocked_matches_flce(N, block):
+    rng = np.random.default_rng(N * 1000 + block)
+    H, V = 24, 301
+    x = rng.standard_normal((N, H))
+    W = rng.standard_normal((V, H)) * 0.6
+    t = rng.integers(0, V, N)
+    want = oracle.flce(x, W, t)
+    got = oracle.flce_blocked(x, W, t, block=block)
+    np.testing.assert_allclose(got["loss"], want["loss"], rtol=1e-14)
+    np.testing.assert_allclose(got["lse"], want["lse"], rtol=1e-14)
+    np.testing.assert_allclose(got["losses"], want["losses"], rtol=1e-13)
+    np.testing.assert_array_equal(got["dx_rows"], np.arange(N))
+    np.testing.assert_allclose(got["dx"], want["dx"], rtol=1e-11, atol=1e-17)
+    np.testing.assert_allclose(got["dW"], want["dW"], rtol=1e-11, atol=1e-17)
+
+
+def test_blocked_storage_forms_and_selected_blocks():
+    """bf16 / fp32 storage widened block by block equals the widened whole; dx of selected blocks."""
+    for dt in ("bf16", "fp32"):
+        d = make_inputs(150, 40, 500, dt, seed=41)
+        want = oracle.flce(oracle.widen(d["x"], dt), oracle.widen(d["W"], dt), d["t"])
+        got = oracle.flce_blocked(d["x"], d["W"], d["t"], block=64, dtype=dt, dx_blocks=[2, 0])
+        assert got["loss"] == pytest.approx(want["loss"], rel=1e-14)
+        rows = np.concatenate([np.arange(0, 64), np.arange(128, 150)])
+        np.testing.assert_array_equal(got["dx_rows"], rows)
+        np.testing.assert_allclose(got["dx"], want["dx"][rows], rtol=1e-11, atol=1e-17)
+        np.testing.assert_allclose(got["dW"], want["dW"], rtol=1e-11, atol=1e-17)
+    seen = []
+    oracle.flce_blocked(d["x"], d["W"], d["t"], block=64, dtype="fp32", dx_blocks=[],
+                        progress=lambda b, n: seen.append((b, n)))
+    assert seen == [(0, 3), (1, 3), (2, 3)]
+
+
+def _blocked_mutant(kind, block=2):
+    """Copies of the blocked loop with one plausible mistake each."""
+    def f(x, W, t):
+        x = np.asarray(x, dtype=np.float64)
+        W = np.asarray(W, dtype=np.float64)
+        t = np.asarray(t, dtype=np.int64)
+        N = x.shape[0]
+        lse, losses = np.empty(N), np.empty(N)
+        dW = np.zeros_like(W)
+        dx = np.zeros_like(x)
+        means = []
+        for s in range(0, N, block):
+            e = min(N, s + block)
+            xb = x[s:e]
+            Z = fo.logits(xb, W)
+            lse[s:e] = fo.row_logsumexp(Z)
+            losses[s:e] = fo.row_losses(Z, t[s:e], lse[s:e])
+            means.append(losses[s:e].mean())
+            G = fo.dlogits(Z, t[s:e], lse[s:e], e - s if kind == "block_local_N" else N)
+            dx[s:e] = G @ W
+            if kind == "dx_rows_shifted" and s > 0:
+                dx[s - 1:e - 1] = G @ W
+            if kind == "dW_overwritten":
+                dW = G.T @ xb
+            else:
+                dW += G.T @ xb
+        loss = float(np.mean(means)) if kind == "mean_of_block_means" else float(losses.mean())
+        return {"loss": loss, "lse": lse, "losses": losses, "dx": dx, "dW": dW}
+    return f
+
+
+BLOCKED_MUTANTS = ["block_local_N", "dx_rows_shifted", "dW_overwritten", "mean_of_block_means"]
+
+
+@pytest.mark.parametrize("kind", BLOCKED_MUTANTS)
+def test_blocked_pins_catch_planted_mistake(kind):
+    bad = _blocked_mutant(kind)
+    caught = []
+    with np.errstate(all="ignore"):
+        for check in pins.ALL_CHECKS:
+            try:
+                check(bad)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {kind!r}"
+
+
+def test_blocked_unmutated_copy_passes():
+    good = _blocked_mutant("none")
+    for check in pins.ALL_CHECKS:
+        check(good)

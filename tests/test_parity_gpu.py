@@ -1,9 +1,9 @@
 """HIP path vs the CPU oracle (GPU only).
 
 Element-wise comparisons at sizes the oracle finishes in seconds (several
-tiles, ragged chunk and vocabulary tails, edge cases), and at the full
-workload sizes in the benchmark's launch configuration: sampled rows against
-the oracle, exact closed forms (W = 0) and invariants that hold at any size.
+tiles, ragged chunk and vocabulary tails, edge cases), and the exact W = 0
+closed form at the Llama-3-vocabulary size (the full-size comparisons with the
+whole oracle are in tests/test_full_size_gpu.py).
 
 Tolerances (written in each assert): loss relative error <= 1e-4; dx and dW
 relative Frobenius error <= 2e-2 for bf16 inputs and <= 1e-5 for fp32 inputs,
@@ -147,51 +147,7 @@ def test_reuse_handle_across_shapes():
     f.close()
 
 
-# ---- full workload sizes, in the benchmark's launch configuration ----------
-
-def _sample_rows(N, C):
-    rows = {0, 1, N - 1, N // 2, C - 1, min(C, N - 1)}
-    rng = np.random.default_rng(N)
-    rows.update(rng.integers(0, N, 10).tolist())
-    return sorted(rows)
-
-
-@pytest.mark.parametrize("name", ["llama2_vocab", "llama3_vocab", "qwen3_vocab", "long_context",
-                                  "llama3_dp8_share", "llama3_tp8_share"])
-def test_full_size_sampled(name):
-    """Full workload size, benchmark launch configuration (bf16 outputs): sampled rows of lse
-    and dx against the oracle, and the loss against its expectation.  Then the same launch
-    with fp32 outputs for the exact invariants, which bf16 outputs cannot show: in a targeted
-    vocabulary row the softmax part of dW (~1/(sqrt(N) V)) is below half a bf16 ulp of the
-    one-hot part (~1/N) and rounds away."""
-    import torch
-    w = WORKLOADS[name]
-    print(f"[full-size] {name} N={w.N} H={w.H} V={w.V} chunk={w.chunk}", flush=True)
-    d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
-    got = run_flce(d, chunk=w.chunk, with_lse=True)
-    got["handle"].close()
-    rows = _sample_rows(w.N, w.chunk)
-    W64 = oracle.widen(d["W"], "bf16")
-    want = oracle.flce_rows(oracle.widen(d["x"][rows], "bf16"), W64, d["t"][rows],
-                            range(len(rows)), w.N)
-    assert np.max(np.abs(got["lse"][rows] - want["lse"])) <= 1e-4 * np.max(np.abs(want["lse"]))
-    assert rel_fro(got["dx"][rows], want["dx"]) <= 2e-2
-    # the loss: statistical expectation for these distributions (ln V + 2e-4 H)
-    assert abs(got["loss"] - (math.log(w.V) + 2e-4 * w.H)) < 0.1
-    del got
-    # exact invariants at any size, fp32 outputs: dW column sums vanish; <x,dx> = <W,dW>
-    g32 = run_flce(d, chunk=w.chunk, dx_dtype=torch.float32, dw_dtype=torch.float32)
-    g32["handle"].close()
-    assert rel_fro(g32["dx"][rows], want["dx"]) <= 2e-2
-    dW = g32["dW"]
-    # each column sum of the softmax part is mean_n x_n (~1/sqrt(N)): a 1% error in the
-    # softmax normalisation would give |colsum| ~ 1e-2 |dW column|
-    assert np.linalg.norm(dW.sum(axis=0)) <= 1e-3 * np.linalg.norm(dW)
-    x64 = oracle.widen(d["x"], "bf16")
-    a = float(np.sum(x64 * g32["dx"]))
-    b = float(np.sum(W64 * dW))
-    assert abs(a - b) <= 1e-3 * max(abs(a), abs(b))
-
+# ---- full workload sizes: tests/test_full_size_gpu.py holds the whole-oracle comparisons ----
 
 def test_full_size_zero_weight_closed_form():
     """W = 0 at the Llama-3-vocabulary size: loss = ln V, dx = 0 and
