@@ -174,6 +174,64 @@ def hipblaslt_yardstick(x, W, rows: int, reps: int = 10):
     return res
 
 
+def fused_record(flce, x, W, t, w, chunk, steps, ignore, reduction):
+    """The fused variant (two passes, no logits buffer) on the same inputs, fp32 gradients (with
+    bf16 dW its fp32 accumulator would be V H 4 bytes extra): ms per step, credited TFLOP/s
+    (6 N H V) and executed (8 N H V: the recompute), peak extra HBM, per-kernel averages."""
+    import torch
+    dev = x.device
+    f = flce.FusedLinearCrossEntropy(in_dtype=x.dtype, dx_dtype=torch.float32, dw_dtype=torch.float32,
+                                     variant=flce.FLCE_FUSED)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dx = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    f.reserve(w.N, w.H, w.V, chunk)
+    ws = f.workspace_bytes(w.N, w.H, w.V, chunk)
+    out = (loss, dx, dW, None)
+
+    def step():
+        f.forward_backward(x, W, t, chunk=chunk, out=out, reduction=reduction, ignore_index=ignore)
+    step()
+    torch.cuda.synchronize()
+    f.profile_enable(True)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    stats = f.profile_read()
+    peak_extra = torch.cuda.max_memory_allocated() - base + ws
+    status = f.check()
+    lval = loss.item()
+    f.close()
+    del dx, dW
+    torch.cuda.empty_cache()
+    if status != 0 or not math.isfinite(lval):
+        raise SystemExit(f"fused bench run is invalid: status {status}, loss {lval}")
+    fl = 6.0 * w.N * w.H * w.V
+    kernels = {}
+    for name, st in stats.items():
+        avg = st["total_ms"] / max(st["launches"], 1)
+        k = {"launches_per_step": st["launches"] / steps, "avg_ms": round(avg, 4)}
+        if st["flops"] > 0:
+            k["tflops_executed"] = round(st["flops"] / st["launches"] / (avg * 1e-3) / 1e12, 1)
+        kernels[name] = k
+    log(f"[bench] fused: {ms:.2f} ms/step, loss {lval:.6f}")
+    return {"variant": "fused", "grad_dtype": "fp32", "steps": steps, "warmup": 1, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.N / (ms * 1e-3), 1),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "mfma_peak_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "tflops_executed": round(8.0 / 6.0 * fl / (ms * 1e-3) / 1e12, 1),
+            "peak_extra_gb": round(peak_extra / 1e9, 3), "workspace_gb": round(ws / 1e9, 3),
+            "loss": round(lval, 6), "kernels": kernels}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,8 +252,11 @@ def main():
                     help="RMSNorm in front of the head (flce_rmsnorm_forward_backward): the workload's x "
                          "becomes the hidden states, gamma ~ 1 + 0.2 N(0,1) (seeded), eps 1e-6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--materialised", action="store_true",
-                    help="also measure the peak HBM of the materialised-logits PyTorch path")
+    ap.add_argument("--no-materialised", action="store_true",
+                    help="skip the peak-HBM measurement of the materialised-logits PyTorch path")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-variant sub-record (fp32 gradients) of a chunked run")
+    ap.add_argument("--fused-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="after the run, copy a buffer of this many GiB once (a plain copy kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -344,9 +405,16 @@ def main():
              "workspace_gb": round(ws_bytes / 1e9, 3),
              "free_delta_gb": round((free0 - free1) / 1e9, 3),
              "materialised_fp32_logits_gb": round(w.N * w.V * 4 / 1e9, 2)}
-    if args.materialised:
-        f.close()
-        del dx, dW
+    f.close()
+    del dx, dW, dgamma, out
+    torch.cuda.empty_cache()
+    fused = None
+    if args.variant == "chunked" and not args.no_fused and not (args.forward_only or args.rmsnorm or
+                                                               args.accumulate or w.dtype != "bf16"):
+        log(f"[bench] fused variant, fp32 gradients: {args.fused_steps} timed steps")
+        fused = fused_record(flce, x, W, t, w, chunk, args.fused_steps, ignore, args.reduction)
+    if not args.no_materialised:
+        log("[bench] peak HBM of the materialised-logits PyTorch loss")
         extra["materialised_baseline"] = materialised_peak(x, W, t)
 
     if args.copy_calibration > 0:
@@ -387,6 +455,8 @@ def main():
         "tflops": round(tflops, 1), "mfma_peak_frac": round(tflops / peak_tf, 4),
         "memory": extra, "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
     }
+    if fused is not None:
+        rec["fused_variant"] = fused
     if yard is not None:
         rec["yardstick_hipblaslt"] = yard
     print(json.dumps(rec), flush=True)

@@ -20,17 +20,33 @@
  * Conventions shared by every entry point:
  *  - All tensors are caller-owned DEVICE pointers on the handle's device,
  *    row-major and contiguous, 16-byte aligned.
- *  - `stream` is a hipStream_t (passed as void*).  Every kernel is enqueued
- *    on it and the call returns after enqueueing: no host synchronisation,
- *    no use of the null stream by the library itself (the stream/event
- *    ordering rules of the async continuous-batching page, pogovet.com).
- *    Results are valid once the stream reaches that point.
+ *  - `stream` is a hipStream_t (passed as void*).  Every kernel of a call is
+ *    enqueued on it and the call returns after enqueueing: the call itself
+ *    neither synchronises the host nor enqueues anything on the null stream
+ *    (the stream and event ordering rules of the async continuous-batching
+ *    page, pogovet.com, "default stream" and "events" sections).  Results
+ *    are valid once the stream reaches that point.  What does synchronise:
+ *    growing the workspace (hipMalloc/hipFree: flce_reserve, or the first call
+ *    that needs more), flce_check (the given stream), flce_profile_read (the
+ *    recorded events, then a blocking copy of the clock counters) and
+ *    flce_destroy (hipFree).
  *  - No output may overlap an input or another output (byte ranges are
  *    compared; INVALID_ARG otherwise): later chunks read x and W after
  *    earlier chunks have written dx and dW.
  *  - Validation happens before any launch; a call that returns an error
  *    writes nothing.  Nothing aborts and no exception crosses the ABI.
- *  - A handle must not be used by two calls at the same time.
+ *  - A handle owns one workspace, shared by all its calls: calls on one
+ *    handle must be ordered on the device (the same stream, or streams
+ *    ordered by events), and a handle must not be used by two host threads
+ *    at the same time.  Distinct handles share nothing.
+ *  - Graph capture: a call captured into a HIP graph enqueues kernels only
+ *    (no memset, no allocation).  Under capture nothing may be allocated, so
+ *    a captured call whose workspace is not yet large enough (flce_reserve it
+ *    first, or run the call once eagerly) fails with UNSUPPORTED.  A graph
+ *    holds the handle's workspace address: after the first captured call the
+ *    workspace is pinned for the handle's lifetime, and a later call or
+ *    flce_reserve that would need a larger one fails with UNSUPPORTED instead
+ *    of moving it.  A captured graph must not be replayed after flce_destroy.
  */
 #ifndef FLCE_H
 #define FLCE_H
@@ -76,12 +92,18 @@ typedef struct {
 
 typedef struct flce_handle_s* flce_handle_t;
 
-/* Creates a handle.  No device memory is allocated yet.
- * Errors: INVALID_ARG (null cfg/out, bad enum), UNSUPPORTED (fp32 inputs with a bf16 output, or
- *         the fused variant with fp32 inputs), HIP (device ordinal not usable). */
+/* Creates a handle: the configuration (dtypes, variant, device) and, later, the workspace that
+ * holds the chunk's logits buffer of the FLCE page's core idea (one [C,V] buffer reused by every
+ * chunk).  The pages define no handle; it is the plumbing of this C interface, which keeps that
+ * buffer between calls instead of allocating it per call.  No device memory is allocated yet.
+ * `*out` receives the handle, owned by the caller until flce_destroy.
+ * Errors: INVALID_ARG (null cfg/out, bad enum, reserved != 0, negative limit or device),
+ *         UNSUPPORTED (fp32 inputs with a bf16 output, or the fused variant with fp32 inputs),
+ *         HIP (device ordinal not usable). */
 flce_status_t flce_create(const flce_config_t* cfg, flce_handle_t* out);
 
-/* Frees the handle's workspace (device-synchronising) and the handle.  NULL is a no-op. */
+/* Frees the handle's workspace and the handle (hipFree: synchronises the device).  Interface
+ * plumbing, like flce_create.  NULL is a no-op.  Always returns FLCE_OK. */
 flce_status_t flce_destroy(flce_handle_t h);
 
 /* One fused forward+backward pass.
@@ -96,7 +118,9 @@ flce_status_t flce_destroy(flce_handle_t h);
  *   dW      [V,H]  cfg.dw_dtype, overwritten
  * The workspace grows on demand (hipMalloc/hipFree, which synchronise the device); call
  * flce_reserve beforehand to keep allocation out of timed or captured regions.
- * Errors: INVALID_ARG, UNSUPPORTED, OOM (outputs untouched), HIP. */
+ * Errors: INVALID_ARG, UNSUPPORTED (also: a captured call or a pinned workspace that would
+ * need to grow), OOM (allocation failed or cfg.workspace_limit exceeded; outputs untouched),
+ * HIP. */
 flce_status_t flce_forward_backward(flce_handle_t h, const void* x, const void* W,
                                     const int64_t* targets, int64_t N, int64_t H, int64_t V,
                                     int64_t chunk, float* loss, void* dx, void* dW, void* stream);
@@ -179,15 +203,26 @@ size_t flce_rmsnorm_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64
  * the chunk's logits buffer stays within 1.5 GB, then clamped to N.  Returns 0 for invalid sizes. */
 int64_t flce_effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk);
 
-/* Workspace bytes a call with these sizes needs (0 for invalid sizes). */
+/* Workspace bytes a call with these sizes needs (0 for invalid sizes or a NULL handle): the
+ * chunk's logits buffer (C x ceil(V/256)*256 elements of the input dtype; the buffer the FLCE
+ * page's core idea overwrites in place with dlogits), the per-row log-sum-exp partials of the
+ * online softmax (the streaming CE kernel of the "Unsloth deep architecture" page: a running
+ * maximum and sum per row and 256-wide vocabulary tile, 8 bytes each), 12 bytes per token (target
+ * logit, lse, loss), and split-K partials of the dx product when the chunk has few output tiles. */
 size_t flce_workspace_bytes(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk);
 
-/* Allocates the workspace for these sizes now (no-op if already large enough).
- * Errors: INVALID_ARG, UNSUPPORTED, OOM, HIP. */
+/* Allocates the workspace for these sizes now (no-op if already large enough); synchronises the
+ * device when it allocates.  Interface plumbing: keeps allocation out of timed or captured calls.
+ * Errors: INVALID_ARG, UNSUPPORTED (sizes; or a pinned workspace that would need to grow), OOM,
+ * HIP. */
 flce_status_t flce_reserve(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk);
 
 /* Synchronises `stream`, then reports and clears the device-side data flag:
- * FLCE_ERR_DATA if any call since the last check saw a target outside [0,V), else FLCE_OK. */
+ * FLCE_ERR_DATA if any call since the last check saw a target outside [0,V), else FLCE_OK.
+ * Targets are class ids in [0, V) (the cross-entropy equation of the "Unsloth deep architecture"
+ * page indexes the logits by the target); a kernel cannot return an error without a host
+ * synchronisation, so an out-of-range id is recorded on the device and reported here.
+ * Errors: INVALID_ARG (NULL handle), HIP. */
 flce_status_t flce_check(flce_handle_t h, void* stream);
 
 /* ---- per-kernel timing (tracing) ----------------------------------------------------
@@ -196,7 +231,10 @@ flce_status_t flce_check(flce_handle_t h, void* stream);
  * the event after it on that stream.  The GEMM kernels (logits_lse, dx, dw) also time each of
  * their workgroups with the shader-clock counter and the 100 MHz real-time counter, whose ratio
  * is the shader clock the GEMMs actually ran at.  Enabling (or disabling) resets the statistics;
- * enabling allocates 2 * 8 bytes of device memory per kernel kind once per handle. */
+ * enabling allocates 2 * 8 bytes of device memory per kernel kind once per handle, which the next
+ * call clears on its stream.  Measurement plumbing (the per-kernel times and flops feed the
+ * roofline: 2 N H V flops per GEMM launch, the forward 2PD and backward 4PD of the compute
+ * section of "Transformer Math 101"). */
 typedef struct {
   char name[32];          /* kernel name, e.g. "logits_lse", "dx", "dw" */
   int64_t launches;       /* launches timed since the last reset */
@@ -211,10 +249,12 @@ flce_status_t flce_profile_enable(flce_handle_t h, int enable);
 
 /* Synchronises on the recorded events, folds them into the statistics and copies up to
  * `capacity` entries (one per kernel that ran) into `out`; `*count` receives the number of
- * entries available.  Errors: INVALID_ARG, HIP. */
+ * entries available.  The clock counters come back by a blocking device-to-host copy.
+ * Errors: INVALID_ARG, HIP. */
 flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int capacity, int* count);
 
-/* Static description of a status code. */
+/* Static description of a status code (never NULL; "unknown flce status" for other values).
+ * Interface plumbing: the error convention of this C interface (status codes, no aborts). */
 const char* flce_status_string(flce_status_t s);
 
 #ifdef __cplusplus

@@ -83,7 +83,10 @@ struct flce_handle_s {
   flce_config_t cfg;
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  int* flag = nullptr;      // device int, bit 0 = out-of-range target seen
+  int* flag = nullptr;      // device int (16 bytes allocated), bit 0 = out-of-range target seen
+  bool flag_ready = false;  // the flag has been cleared by a kernel on a caller's stream
+  bool ws_pinned = false;   // a call was captured into a graph: the workspace may no longer move
+  bool clk_reset = false;   // the clock counters are cleared before the next profiled launch
   bool profiling = false;
   unsigned long long* clk = nullptr;   // device [K_COUNT][2]: GEMM workgroup lifetimes (shader, 100 MHz ticks)
   std::vector<Mark> marks;  // pending events, in stream order
@@ -109,14 +112,24 @@ struct DeviceGuard {
   }
 };
 
+// What one call runs with: its handle, the device memory it works in (the handle's workspace, or
+// the no-allocation scratch), the data flag it raises, and whether it is traced.
+struct Exec {
+  flce_handle_s* h;
+  char* ws;
+  int* flag;
+  bool prof;
+};
+
 // The device clock counters of a GEMM kernel kind while profiling, else null.
-unsigned long long* clock_of(flce_handle_s* h, int kind) {
-  return h->profiling && h->clk != nullptr ? h->clk + 2 * kind : nullptr;
+unsigned long long* clock_of(const Exec& e, int kind) {
+  return e.prof && e.h->clk != nullptr ? e.h->clk + 2 * kind : nullptr;
 }
 
 // Records a profiling event before a launch of `kind` (or kind -1 after the last launch).
-hipError_t mark(flce_handle_s* h, int kind, double flops, double bytes, hipStream_t st) {
-  if (!h->profiling) return hipSuccess;
+hipError_t mark(const Exec& e, int kind, double flops, double bytes, hipStream_t st) {
+  if (!e.prof) return hipSuccess;
+  flce_handle_s* h = e.h;
   hipEvent_t ev;
   if (!h->pool.empty()) {
     ev = h->pool.back();
@@ -265,20 +278,23 @@ bool outputs_disjoint(std::initializer_list<Span> in, std::initializer_list<Span
   return true;
 }
 
+// Allocates (or grows) the workspace and the data flag.  Nothing is enqueued on any stream: the
+// flag is cleared by the next call's first kernel on the caller's stream (prepare_call).  Once a
+// call has been captured into a graph the workspace is pinned, since the graph holds its address.
 flce_status_t ensure_workspace(flce_handle_s* h, size_t need) {
   if (h->cfg.workspace_limit > 0 && need > (size_t)h->cfg.workspace_limit) return FLCE_ERR_OOM;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
   if (h->flag == nullptr) {
-    if (hipMalloc(reinterpret_cast<void**>(&h->flag), sizeof(int)) != hipSuccess) {
+    if (hipMalloc(reinterpret_cast<void**>(&h->flag), 16) != hipSuccess) {
       h->flag = nullptr;
       (void)hipGetLastError();
       return FLCE_ERR_OOM;
     }
-    const int zero = 0;
-    if (hipMemcpy(h->flag, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return FLCE_ERR_HIP;
+    h->flag_ready = false;
   }
   if (need <= h->ws_bytes) return FLCE_OK;
+  if (h->ws_pinned) return FLCE_ERR_UNSUPPORTED;
   void* p = nullptr;
   if (hipMalloc(&p, need) != hipSuccess) {
     (void)hipGetLastError();
@@ -313,15 +329,46 @@ flce_status_t validate_sizes(const flce_config_t& cfg, int64_t N, int64_t H, int
     if ((call) != hipSuccess) return FLCE_ERR_HIP; \
   } while (0)
 
+// Checks a call against graph capture before anything is enqueued: under capture nothing may be
+// allocated, so the workspace (and flag) must already hold the plan; the workspace is then pinned
+// for the handle's lifetime.  Call before ensure_workspace.
+flce_status_t capture_check(flce_handle_s* h, size_t need, hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return FLCE_ERR_HIP;
+  }
+  if (cs == hipStreamCaptureStatusNone) return FLCE_OK;
+  if (h->flag == nullptr || h->ws == nullptr || need > h->ws_bytes) return FLCE_ERR_UNSUPPORTED;
+  h->ws_pinned = true;
+  return FLCE_OK;
+}
+
+// First kernels of a call, on its stream: clear the data flag after its allocation and the clock
+// counters after profiling was (re-)enabled.
+flce_status_t prepare_call(flce_handle_s* h, hipStream_t st) {
+  if (!h->flag_ready) {
+    flce::FillArgs z{reinterpret_cast<float*>(h->flag), 4};
+    FLCE_LAUNCH(flce::launch_fill_zero(z, st));
+    h->flag_ready = true;
+  }
+  if (h->profiling && h->clk_reset && h->clk != nullptr) {
+    flce::FillArgs z{reinterpret_cast<float*>(h->clk), (int64_t)(2 * K_COUNT * sizeof(unsigned long long) / 4)};
+    FLCE_LAUNCH(flce::launch_fill_zero(z, st));
+    h->clk_reset = false;
+  }
+  return FLCE_OK;
+}
+
 // Token count and normalisation of the call, on the device (no host synchronisation).
-flce_status_t launch_scale(flce_handle_s* h, const Plan& p, const Opts& o, const int64_t* t, hipStream_t st) {
+flce_status_t launch_scale(const Exec& e, const Plan& p, const Opts& o, const int64_t* t, hipStream_t st) {
   flce::ScaleArgs sa{};
   sa.t = t;
   sa.n = p.N;
   sa.ign = o.ign;
   sa.sum = o.sum;
-  sa.out = reinterpret_cast<flce::Scale*>(static_cast<char*>(h->ws) + p.off_scale);
-  FLCE_LAUNCH(mark(h, K_SCALE, 0.0, 8.0 * p.N, st));
+  sa.out = reinterpret_cast<flce::Scale*>(e.ws + p.off_scale);
+  FLCE_LAUNCH(mark(e, K_SCALE, 0.0, 8.0 * p.N, st));
   FLCE_LAUNCH(flce::launch_scale(sa, st));
   return FLCE_OK;
 }
@@ -335,12 +382,12 @@ struct DxOut {
 
 // One chunk of the token-chunked path: logits + statistics, combine, and (with gradients)
 // dlogits, dx rows of the chunk, dW update.  x_c: the chunk's first row of x.
-flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t s, int rows, const void* x_c,
+flce_status_t chunk_flce(const Exec& e, const Plan& p, const Opts& o, int64_t s, int rows, const void* x_c,
                          const void* W, const int64_t* t, float* lse, const DxOut& dxo, void* dW, hipStream_t st) {
-  const flce_config_t& cfg = h->cfg;
+  const flce_config_t& cfg = e.h->cfg;
   const In in = cfg.in_dtype == FLCE_BF16 ? In::BF16 : In::FP32;
   const size_t es = in_size(cfg);
-  char* ws = static_cast<char*>(h->ws);
+  char* ws = e.ws;
   void* z = ws + p.off_z;
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
   float* ps = reinterpret_cast<float*>(ws + p.off_ps);
@@ -370,8 +417,8 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   la.V = (int)p.V;
   la.tiles_m = tiles_m;
   la.tiles_n = p.tiles_v;
-  la.clk = clock_of(h, K_LOGITS);
-  FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
+  la.clk = clock_of(e, K_LOGITS);
+  FLCE_LAUNCH(mark(e, K_LOGITS, gemm_flops, (double)rows * p.H * b_in + VH * b_in + zbytes, st));
   FLCE_LAUNCH(flce::launch_logits(in, la, st));
 
   flce::CombineArgs ca{};
@@ -381,13 +428,13 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   ca.t = t + s;
   ca.lse = lse + s;
   ca.loss_rows = loss_rows + s;
-  ca.flag = h->flag;
+  ca.flag = e.flag;
   ca.ign = o.ign;
   ca.pstride = (int)p.C;
   ca.tiles_n = p.tiles_v;
   ca.rows = rows;
   ca.V = (int)p.V;
-  FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
+  FLCE_LAUNCH(mark(e, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
   FLCE_LAUNCH(flce::launch_combine(ca, st));
   if (!o.grads) return FLCE_OK;
 
@@ -402,7 +449,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   ga.V = (int)p.V;
   ga.ign = o.ign;
   ga.scale = scale;
-  FLCE_LAUNCH(mark(h, K_DLOGITS, 0.0, 2.0 * zbytes + 4.0 * rows * p.tiles_v, st));
+  FLCE_LAUNCH(mark(e, K_DLOGITS, 0.0, 2.0 * zbytes + 4.0 * rows * p.tiles_v, st));
   FLCE_LAUNCH(flce::launch_dlogits(in, ga, st));
 
   flce::DxArgs xa{};
@@ -421,8 +468,8 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   xa.tiles_n = p.tiles_h;
   xa.dx_fp32 = dxo.fp32;
   xa.accumulate = dxo.accumulate;
-  xa.clk = clock_of(h, K_DX);
-  FLCE_LAUNCH(mark(h, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
+  xa.clk = clock_of(e, K_DX);
+  FLCE_LAUNCH(mark(e, K_DX, gemm_flops, zbytes + VH * b_in + (double)rows * p.H * b_dx, st));
   FLCE_LAUNCH(flce::launch_dx(in, xa, st));
   if (p.splits > 1) {
     flce::DxReduceArgs ra{};
@@ -433,7 +480,7 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
     ra.splits = p.splits;
     ra.dx_fp32 = xa.dx_fp32;
     ra.accumulate = xa.accumulate;
-    FLCE_LAUNCH(mark(h, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
+    FLCE_LAUNCH(mark(e, K_DX_REDUCE, 0.0, (double)rows * p.H * (4.0 * p.splits + b_dx), st));
     FLCE_LAUNCH(flce::launch_dx_reduce(ra, st));
   }
 
@@ -449,58 +496,58 @@ flce_status_t chunk_flce(flce_handle_s* h, const Plan& p, const Opts& o, int64_t
   wa.tiles_n = p.tiles_h;
   wa.dw_fp32 = cfg.dw_dtype == FLCE_FP32;
   wa.accumulate = s > 0 || o.accumulate;
-  wa.clk = clock_of(h, K_DW);
-  FLCE_LAUNCH(mark(h, K_DW, gemm_flops,
+  wa.clk = clock_of(e, K_DW);
+  FLCE_LAUNCH(mark(e, K_DW, gemm_flops,
                    zbytes + (double)rows * p.H * b_in + VH * b_dw * (wa.accumulate ? 2.0 : 1.0), st));
   FLCE_LAUNCH(flce::launch_dw(in, wa, st));
   return FLCE_OK;
 }
 
-flce_status_t finalize_loss(flce_handle_s* h, const Plan& p, float* loss, hipStream_t st) {
-  char* ws = static_cast<char*>(h->ws);
+flce_status_t finalize_loss(const Exec& e, const Plan& p, float* loss, hipStream_t st) {
+  char* ws = e.ws;
   flce::FinalizeArgs fa{};
   fa.loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   fa.loss = loss;
   fa.n = p.N;
   fa.scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
-  FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
+  FLCE_LAUNCH(mark(e, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
   FLCE_LAUNCH(flce::launch_finalize(fa, st));
   return FLCE_OK;
 }
 
-flce_status_t run_chunked(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
+flce_status_t run_chunked(const Exec& e, const Plan& p, const Opts& o, const void* x, const void* W,
                           const int64_t* t, float* loss, void* dx, void* dW, float* lse_out,
                           hipStream_t st) {
-  const flce_config_t& cfg = h->cfg;
+  const flce_config_t& cfg = e.h->cfg;
   const size_t es = in_size(cfg);
   const size_t dx_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
-  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(static_cast<char*>(h->ws) + p.off_lse);
-  flce_status_t r = launch_scale(h, p, o, t, st);
+  float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(e.ws + p.off_lse);
+  flce_status_t r = launch_scale(e, p, o, t, st);
   if (r != FLCE_OK) return r;
   for (int64_t s = 0; s < p.N; s += p.C) {
     const int rows = (int)std::min(p.C, p.N - s);
     const DxOut dxo{o.grads ? static_cast<char*>(dx) + (size_t)s * p.H * dx_es : nullptr,
                     cfg.dx_dtype == FLCE_FP32, o.accumulate};
-    r = chunk_flce(h, p, o, s, rows, static_cast<const char*>(x) + (size_t)s * p.H * es, W, t, lse, dxo, dW, st);
+    r = chunk_flce(e, p, o, s, rows, static_cast<const char*>(x) + (size_t)s * p.H * es, W, t, lse, dxo, dW, st);
     if (r != FLCE_OK) return r;
   }
-  r = finalize_loss(h, p, loss, st);
+  r = finalize_loss(e, p, loss, st);
   if (r != FLCE_OK) return r;
-  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  FLCE_LAUNCH(mark(e, -1, 0.0, 0.0, st));
   return FLCE_OK;
 }
 
 // RMSNorm in front of the head, per chunk: x_c = rmsnorm(h_c) into the workspace, the FLCE
 // chunk with its dx rows in an fp32 workspace buffer, then dh rows and dgamma partials from
 // them; dgamma is summed in fp32 across chunks and written (or added) in its dtype at the end.
-flce_status_t run_rmsnorm(flce_handle_s* h, const Plan& p, const Opts& o, const void* hid, const void* gamma,
+flce_status_t run_rmsnorm(const Exec& e, const Plan& p, const Opts& o, const void* hid, const void* gamma,
                           float eps, const void* W, const int64_t* t, float* loss, void* dh, void* dgamma,
                           void* dW, float* lse_out, hipStream_t st) {
-  const flce_config_t& cfg = h->cfg;
+  const flce_config_t& cfg = e.h->cfg;
   const In in = cfg.in_dtype == FLCE_BF16 ? In::BF16 : In::FP32;
   const size_t es = in_size(cfg);
   const size_t dh_es = cfg.dx_dtype == FLCE_BF16 ? 2 : 4;
-  char* ws = static_cast<char*>(h->ws);
+  char* ws = e.ws;
   float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   void* xc = ws + p.off_xc;
   float* dxc = reinterpret_cast<float*>(ws + p.off_dxc);
@@ -509,48 +556,48 @@ flce_status_t run_rmsnorm(flce_handle_s* h, const Plan& p, const Opts& o, const 
   const bool dg32 = cfg.dw_dtype == FLCE_FP32;
   float* dg_acc = dg32 ? static_cast<float*>(dgamma) : reinterpret_cast<float*>(ws + p.off_dgacc);
   const double H = (double)p.H;
-  flce_status_t r = launch_scale(h, p, o, t, st);
+  flce_status_t r = launch_scale(e, p, o, t, st);
   if (r != FLCE_OK) return r;
   if (o.grads && !(dg32 && o.accumulate)) {   // fp32 dgamma is its own accumulator
     flce::FillArgs zg{dg_acc, p.H};
-    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * H, st));
+    FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * H, st));
     FLCE_LAUNCH(flce::launch_fill_zero(zg, st));
   }
   for (int64_t s = 0; s < p.N; s += p.C) {
     const int rows = (int)std::min(p.C, p.N - s);
     const void* hc = static_cast<const char*>(hid) + (size_t)s * p.H * es;
     flce::RmsFwdArgs fa{hc, gamma, xc, rstd, rows, (int)p.H, eps};
-    FLCE_LAUNCH(mark(h, K_RMS_FWD, 0.0, (2.0 * rows + 1.0) * H * (double)es + 4.0 * rows, st));
+    FLCE_LAUNCH(mark(e, K_RMS_FWD, 0.0, (2.0 * rows + 1.0) * H * (double)es + 4.0 * rows, st));
     FLCE_LAUNCH(flce::launch_rms_fwd(in, fa, st));
-    r = chunk_flce(h, p, o, s, rows, xc, W, t, lse, DxOut{dxc, true, false}, dW, st);
+    r = chunk_flce(e, p, o, s, rows, xc, W, t, lse, DxOut{dxc, true, false}, dW, st);
     if (r != FLCE_OK) return r;
     if (!o.grads) continue;
     const int nblk = (int)cdiv(rows, flce::kRmsRowsPerBlock);
     flce::RmsBwdArgs ba{dxc, hc, gamma, rstd, static_cast<char*>(dh) + (size_t)s * p.H * dh_es, rpart,
                         rows, (int)p.H, cfg.dx_dtype == FLCE_FP32, o.accumulate};
-    FLCE_LAUNCH(mark(h, K_RMS_BWD, 0.0, rows * H * (4.0 + (double)es + (double)dh_es) + nblk * H * 4.0, st));
+    FLCE_LAUNCH(mark(e, K_RMS_BWD, 0.0, rows * H * (4.0 + (double)es + (double)dh_es) + nblk * H * 4.0, st));
     FLCE_LAUNCH(flce::launch_rms_bwd(in, ba, st));
     flce::RmsReduceArgs ra{rpart, dg_acc, nblk, (int)p.H};
-    FLCE_LAUNCH(mark(h, K_RMS_REDUCE, 0.0, (nblk + 2.0) * H * 4.0, st));
+    FLCE_LAUNCH(mark(e, K_RMS_REDUCE, 0.0, (nblk + 2.0) * H * 4.0, st));
     FLCE_LAUNCH(flce::launch_rms_reduce(ra, st));
   }
   if (o.grads && !dg32) {
     flce::CastArgs cg{dg_acc, dgamma, p.H, o.accumulate};
-    FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * H, st));
+    FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * H, st));
     FLCE_LAUNCH(flce::launch_cast_bf16(cg, st));
   }
-  r = finalize_loss(h, p, loss, st);
+  r = finalize_loss(e, p, loss, st);
   if (r != FLCE_OK) return r;
-  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  FLCE_LAUNCH(mark(e, -1, 0.0, 0.0, st));
   return FLCE_OK;
 }
 
 // Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and pass 2
 // (recompute, dlogits in LDS, dx and dW partials by fp32 atomics); outputs converted last.
-flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const void* x, const void* W,
+flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void* x, const void* W,
                         const int64_t* t, float* loss, void* dx, void* dW, float* lse_out, hipStream_t st) {
-  const flce_config_t& cfg = h->cfg;
-  char* ws = static_cast<char*>(h->ws);
+  const flce_config_t& cfg = e.h->cfg;
+  char* ws = e.ws;
   float* pm = reinterpret_cast<float*>(ws + p.off_pm);
   float* ps = reinterpret_cast<float*>(ws + p.off_ps);
   float* zt = reinterpret_cast<float*>(ws + p.off_zt);
@@ -560,13 +607,13 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
   float* dw_acc = dw32 ? static_cast<float*>(dW) : reinterpret_cast<float*>(ws + p.off_dwacc);
   const flce::Scale* scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
   const double VH = (double)p.V * (double)p.H;
-  const flce_status_t sc = launch_scale(h, p, o, t, st);
+  const flce_status_t sc = launch_scale(e, p, o, t, st);
   if (sc != FLCE_OK) return sc;
 
   // fp32 outputs are the accumulators themselves: cleared unless the call accumulates into them
   if (o.grads && !(dw32 && o.accumulate)) {
     flce::FillArgs zw{dw_acc, p.V * p.H};
-    FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * VH, st));
+    FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * VH, st));
     FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
   }
   for (int64_t s = 0; s < p.N; s += p.C) {
@@ -590,8 +637,8 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
     la.V = (int)p.V;
     la.tiles_m = tiles_m;
     la.tiles_n = p.tiles_v;
-    la.clk = clock_of(h, K_LOGITS);
-    FLCE_LAUNCH(mark(h, K_LOGITS, gemm_flops, (double)rows * p.H * 2 + VH * 2, st));
+    la.clk = clock_of(e, K_LOGITS);
+    FLCE_LAUNCH(mark(e, K_LOGITS, gemm_flops, (double)rows * p.H * 2 + VH * 2, st));
     FLCE_LAUNCH(flce::launch_logits(In::BF16, la, st));
 
     flce::CombineArgs ca{};
@@ -601,20 +648,20 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
     ca.t = t + s;
     ca.lse = lse + s;
     ca.loss_rows = loss_rows + s;
-    ca.flag = h->flag;
+    ca.flag = e.flag;
     ca.ign = o.ign;
     ca.pstride = (int)p.C;
     ca.tiles_n = p.tiles_v;
     ca.rows = rows;
     ca.V = (int)p.V;
-    FLCE_LAUNCH(mark(h, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
+    FLCE_LAUNCH(mark(e, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
     FLCE_LAUNCH(flce::launch_combine(ca, st));
     if (!o.grads) continue;
 
     float* dx_acc = dx32 ? static_cast<float*>(dx) + (size_t)s * p.H : reinterpret_cast<float*>(ws + p.off_dxacc);
     if (!(dx32 && o.accumulate)) {
       flce::FillArgs zx{dx_acc, (int64_t)rows * p.H};
-      FLCE_LAUNCH(mark(h, K_FILL, 0.0, 4.0 * rows * p.H, st));
+      FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
     }
 
@@ -634,17 +681,17 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
     fa.ign = o.ign;
     fa.scale = scale;
     // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
-    FLCE_LAUNCH(mark(h, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
+    FLCE_LAUNCH(mark(e, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
     FLCE_LAUNCH(flce::launch_fused_bwd(fa, st));
     if (!dx32) {
       flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
-      FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * rows * p.H, st));
+      FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_cast_bf16(cx, st));
     }
   }
   if (o.grads && !dw32) {
     flce::CastArgs cw{dw_acc, dW, p.V * p.H, o.accumulate};
-    FLCE_LAUNCH(mark(h, K_CAST, 0.0, 6.0 * VH, st));
+    FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * VH, st));
     FLCE_LAUNCH(flce::launch_cast_bf16(cw, st));
   }
   flce::FinalizeArgs fa{};
@@ -652,9 +699,9 @@ flce_status_t run_fused(flce_handle_s* h, const Plan& p, const Opts& o, const vo
   fa.loss = loss;
   fa.n = p.N;
   fa.scale = scale;
-  FLCE_LAUNCH(mark(h, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
+  FLCE_LAUNCH(mark(e, K_FINALIZE, 0.0, 4.0 * p.N + 4.0, st));
   FLCE_LAUNCH(flce::launch_finalize(fa, st));
-  FLCE_LAUNCH(mark(h, -1, 0.0, 0.0, st));
+  FLCE_LAUNCH(mark(e, -1, 0.0, 0.0, st));
   return FLCE_OK;
 }
 
@@ -782,13 +829,18 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
       return FLCE_ERR_INVALID_ARG;
   }
   const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads);
-  const flce_status_t ws = ensure_workspace(h, p.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  flce_status_t ws = capture_check(h, p.total, st);
+  if (ws != FLCE_OK) return ws;
+  ws = ensure_workspace(h, p.total);
   if (ws != FLCE_OK) return ws;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.fused) return run_fused(h, p, o, x, W, targets, loss, dx, dW, lse, st);
-  return run_chunked(h, p, o, x, W, targets, loss, dx, dW, lse, st);
+  ws = prepare_call(h, st);
+  if (ws != FLCE_OK) return ws;
+  const Exec e{h, static_cast<char*>(h->ws), h->flag, h->profiling};
+  if (p.fused) return run_fused(e, p, o, x, W, targets, loss, dx, dW, lse, st);
+  return run_chunked(e, p, o, x, W, targets, loss, dx, dW, lse, st);
 }
 
 
@@ -829,12 +881,17 @@ flce_status_t flce_rmsnorm_forward_backward(flce_handle_t h, const void* hidden,
       return FLCE_ERR_INVALID_ARG;
   }
   const Plan p = make_plan(h->cfg, N, H, V, chunk, o.grads, true);
-  const flce_status_t ws = ensure_workspace(h, p.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  flce_status_t ws = capture_check(h, p.total, st);
+  if (ws != FLCE_OK) return ws;
+  ws = ensure_workspace(h, p.total);
   if (ws != FLCE_OK) return ws;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
-  return run_rmsnorm(h, p, o, hidden, gamma, eps, W, targets, loss, dhidden, dgamma, dW, lse,
-                     static_cast<hipStream_t>(stream));
+  ws = prepare_call(h, st);
+  if (ws != FLCE_OK) return ws;
+  const Exec e{h, static_cast<char*>(h->ws), h->flag, h->profiling};
+  return run_rmsnorm(e, p, o, hidden, gamma, eps, W, targets, loss, dhidden, dgamma, dW, lse, st);
 }
 
 flce_status_t flce_forward_backward_ex(flce_handle_t h, const void* x, const void* W,
@@ -863,8 +920,7 @@ flce_status_t flce_profile_enable(flce_handle_t h, int enable) {
       (void)hipGetLastError();
       return FLCE_ERR_OOM;
     }
-    const std::vector<unsigned long long> zero(2 * K_COUNT, 0ull);
-    if (hipMemcpy(h->clk, zero.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) return FLCE_ERR_HIP;
+    h->clk_reset = true;   // cleared by the next call's first kernel, on its stream
   }
   h->profiling = enable != 0;
   return FLCE_OK;
@@ -877,7 +933,7 @@ flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int ca
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
   hipError_t e = fold_marks(h);
   unsigned long long clk[2 * K_COUNT] = {};
-  if (h->clk != nullptr) {
+  if (h->clk != nullptr && !h->clk_reset) {   // blocking copy (null stream) of the clock counters
     const hipError_t e2 = hipMemcpy(clk, h->clk, sizeof(clk), hipMemcpyDeviceToHost);
     if (e2 != hipSuccess) e = e2;
   }
@@ -903,7 +959,7 @@ flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int ca
 
 flce_status_t flce_check(flce_handle_t h, void* stream) {
   if (h == nullptr) return FLCE_ERR_INVALID_ARG;
-  if (h->flag == nullptr) return FLCE_OK;
+  if (h->flag == nullptr || !h->flag_ready) return FLCE_OK;   // no call has run on this handle yet
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
