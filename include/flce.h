@@ -167,6 +167,27 @@ flce_status_t flce_forward_backward_opt(flce_handle_t h, const void* x, const vo
                                         int64_t chunk, const flce_options_t* opt, float* loss, void* dx,
                                         void* dW, float* lse, void* stream);
 
+/* flce_forward_backward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It calls no hipMalloc, hipFree
+ * or allocating library routine: the call's workspace lives in a library-owned array of 256 MiB
+ * per device (a static __device__ array, `scratch`; each GPU the library runs on holds its own
+ * copy until the process ends), whose address is looked up once per device by the first such
+ * call on it (hipGetSymbolAddress; make that first call outside graph capture).
+ *   Arguments, layouts, results and errors as for flce_forward_backward; chunked variant only
+ *   (UNSUPPORTED for a fused handle).  The handle's own workspace is not used.
+ *   chunk > 0: used as given (clamped to N); the call fails with UNSUPPORTED, writing nothing, if
+ *     its workspace (flce_workspace_bytes for that chunk) exceeds 256 MiB - 256 bytes.
+ *   chunk <= 0: the automatic chunk (flce_effective_chunk), halved until the workspace fits (512
+ *     tokens at V = 128,256, H = 4,096; a smaller chunk re-reads W more often, so such calls are
+ *     slower); UNSUPPORTED if not even one token fits (12 bytes per token of N are needed too).
+ * Every call on a GPU uses that GPU's one array and leaves its contents behind: calls on the
+ * same device that overlap in time (on different streams, through any handle) race and give
+ * wrong results; order them on the device.  An out-of-range target raises a flag in the array
+ * that flce_check of any handle on that device reports (and clears).  No profiling events. */
+flce_status_t flce_forward_backward_noalloc(flce_handle_t h, const void* x, const void* W,
+                                            const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                            int64_t chunk, float* loss, void* dx, void* dW, void* stream);
+
 /* Workspace bytes a flce_forward_backward_opt call with these sizes and options needs (0 for
  * invalid sizes or options); forward only needs no logits buffer and no gradient accumulators. */
 size_t flce_workspace_bytes_opt(flce_handle_t h, int64_t N, int64_t H, int64_t V, int64_t chunk,

@@ -18,7 +18,7 @@ from typing import Optional
 __all__ = [
     "FLCE_BF16", "FLCE_FP32", "FLCE_CHUNKED", "FLCE_FUSED", "STATUS", "FlceError", "Config",
     "library_path", "load_library", "flce_create", "flce_destroy", "flce_forward_backward",
-    "flce_forward_backward_ex", "flce_forward_backward_opt", "Options", "FLCE_MEAN", "FLCE_SUM",
+    "flce_forward_backward_ex", "flce_forward_backward_opt", "flce_forward_backward_noalloc", "Options", "FLCE_MEAN", "FLCE_SUM",
     "FLCE_ACCUMULATE", "FLCE_FORWARD_ONLY", "flce_effective_chunk", "flce_workspace_bytes", "flce_workspace_bytes_opt", "flce_reserve",
     "flce_rmsnorm_forward_backward", "flce_rmsnorm_workspace_bytes",
     "flce_check", "flce_status_string", "flce_profile_enable", "flce_profile_read", "KernelStat",
@@ -91,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     lib.flce_forward_backward_opt.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.POINTER(Options),
                                               vp, vp, vp, vp, vp]
     lib.flce_forward_backward_opt.restype = i32
+    lib.flce_forward_backward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp]
+    lib.flce_forward_backward_noalloc.restype = i32
     lib.flce_effective_chunk.argtypes = [i64, i64, i64, i64]
     lib.flce_effective_chunk.restype = i64
     lib.flce_workspace_bytes.argtypes = [vp, i64, i64, i64, i64]
@@ -148,6 +150,11 @@ def flce_forward_backward_opt(handle, x, W, targets, N, H, V, chunk, opt, loss, 
     return load_library().flce_forward_backward_opt(handle, x, W, targets, N, H, V, chunk,
                                                     ctypes.byref(opt) if opt is not None else None,
                                                     loss, dx, dW, lse, stream)
+
+
+def flce_forward_backward_noalloc(handle, x, W, targets, N, H, V, chunk, loss, dx, dW, stream) -> int:
+    return load_library().flce_forward_backward_noalloc(handle, x, W, targets, N, H, V, chunk, loss, dx, dW,
+                                                        stream)
 
 
 def flce_effective_chunk(N, H, V, chunk) -> int:

@@ -16,6 +16,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -732,6 +733,52 @@ flce_status_t validate_rmsnorm(const flce_config_t& cfg, int64_t H, float eps) {
 
 }  // namespace
 
+// ---- device memory of the no-allocation entry point ------------------------------------------
+// One array per device (the code object's copy on each GPU it is loaded on, held until the process
+// ends).  Bytes [0, 256) hold the data flag (zero at load, cleared again by flce_check), the rest
+// the call's workspace.  In host code `scratch` is a host-side stand-in, not a device address:
+// only the address hipGetSymbolAddress returns for a device is ever passed to a kernel.
+namespace {
+constexpr size_t kScratchBytes = (size_t)256 << 20;   // 256 MiB
+constexpr size_t kScratchFlagBytes = 256;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev`, looked up once per device (with that device
+// current) and kept; null if it has not been looked up (lookup = false) or the lookup failed.
+char* scratch_on(int dev, bool lookup) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr && lookup) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = static_cast<char*>(p);
+  }
+  return g_scratch[dev];
+}
+
+// Chunk of a no-allocation call: a positive chunk as given (clamped to N); otherwise the
+// automatic chunk, halved until the call's workspace fits the scratch.  0 if nothing fits.
+int64_t noalloc_chunk(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk) {
+  const size_t cap = kScratchBytes - kScratchFlagBytes;
+  int64_t c = effective_chunk(N, H, V, chunk, (int64_t)in_size(cfg));
+  if (chunk > 0) return make_plan(cfg, N, H, V, c).total <= cap ? c : 0;
+  while (c > 1 && make_plan(cfg, N, H, V, c).total > cap) c = (c + 1) / 2;
+  return make_plan(cfg, N, H, V, c).total <= cap ? c : 0;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* flce_status_string(flce_status_t s) {
@@ -907,6 +954,36 @@ flce_status_t flce_forward_backward(flce_handle_t h, const void* x, const void* 
   return flce_forward_backward_opt(h, x, W, targets, N, H, V, chunk, nullptr, loss, dx, dW, nullptr, stream);
 }
 
+flce_status_t flce_forward_backward_noalloc(flce_handle_t h, const void* x, const void* W,
+                                            const int64_t* targets, int64_t N, int64_t H, int64_t V,
+                                            int64_t chunk, float* loss, void* dx, void* dW, void* stream) {
+  if (h == nullptr || x == nullptr || W == nullptr || targets == nullptr || loss == nullptr || dx == nullptr ||
+      dW == nullptr)
+    return FLCE_ERR_INVALID_ARG;
+  if (h->cfg.variant != FLCE_CHUNKED) return FLCE_ERR_UNSUPPORTED;
+  const flce_status_t v = validate_sizes(h->cfg, N, H, V, chunk);
+  if (v != FLCE_OK) return v;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(dx) || !aligned16(dW) ||
+      (reinterpret_cast<uintptr_t>(targets) & 7u) || (reinterpret_cast<uintptr_t>(loss) & 3u))
+    return FLCE_ERR_UNSUPPORTED;
+  {
+    const int64_t es = (int64_t)in_size(h->cfg);
+    const int64_t dx_es = h->cfg.dx_dtype == FLCE_BF16 ? 2 : 4, dw_es = h->cfg.dw_dtype == FLCE_BF16 ? 2 : 4;
+    if (!outputs_disjoint({Span(x, N * H * es), Span(W, V * H * es), Span(targets, N * 8)},
+                          {Span(loss, 4), Span(dx, N * H * dx_es), Span(dW, V * H * dw_es)}))
+      return FLCE_ERR_INVALID_ARG;
+  }
+  const int64_t C = noalloc_chunk(h->cfg, N, H, V, chunk);
+  if (C == 0) return FLCE_ERR_UNSUPPORTED;   // the call's workspace exceeds the scratch
+  const Plan p = make_plan(h->cfg, N, H, V, C);
+  DeviceGuard g(h->cfg.device);
+  if (g.err != hipSuccess) return FLCE_ERR_HIP;
+  char* base = scratch_on(h->cfg.device, true);
+  if (base == nullptr) return FLCE_ERR_HIP;
+  const Exec e{h, base + kScratchFlagBytes, reinterpret_cast<int*>(base), false};
+  return run_chunked(e, p, Opts{}, x, W, targets, loss, dx, dW, nullptr, static_cast<hipStream_t>(stream));
+}
+
 flce_status_t flce_profile_enable(flce_handle_t h, int enable) {
   if (h == nullptr) return FLCE_ERR_INVALID_ARG;
   DeviceGuard g(h->cfg.device);
@@ -959,20 +1036,28 @@ flce_status_t flce_profile_read(flce_handle_t h, flce_kernel_stat_t* out, int ca
 
 flce_status_t flce_check(flce_handle_t h, void* stream) {
   if (h == nullptr) return FLCE_ERR_INVALID_ARG;
-  if (h->flag == nullptr || !h->flag_ready) return FLCE_OK;   // no call has run on this handle yet
+  // the handle's flag (once a call has cleared it) and the device's no-allocation flag (once a
+  // no-allocation call has run on the device)
+  int* flags[2] = {h->flag != nullptr && h->flag_ready ? h->flag : nullptr,
+                   reinterpret_cast<int*>(scratch_on(h->cfg.device, false))};
+  if (flags[0] == nullptr && flags[1] == nullptr) return FLCE_OK;
   DeviceGuard g(h->cfg.device);
   if (g.err != hipSuccess) return FLCE_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int f = 0;
-  if (hipMemcpyAsync(&f, h->flag, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return FLCE_ERR_HIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
-  if (f != 0) {
-    const int zero = 0;
-    if (hipMemcpyAsync(h->flag, &zero, sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) return FLCE_ERR_HIP;
+  bool bad = false;
+  for (int* fl : flags) {
+    if (fl == nullptr) continue;
+    int f = 0;
+    if (hipMemcpyAsync(&f, fl, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return FLCE_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
-    return FLCE_ERR_DATA;
+    if (f != 0) {
+      const int zero = 0;
+      if (hipMemcpyAsync(fl, &zero, sizeof(int), hipMemcpyHostToDevice, st) != hipSuccess) return FLCE_ERR_HIP;
+      if (hipStreamSynchronize(st) != hipSuccess) return FLCE_ERR_HIP;
+      bad = true;
+    }
   }
-  return FLCE_OK;
+  return bad ? FLCE_ERR_DATA : FLCE_OK;
 }
 
 }  // extern "C"
