@@ -72,8 +72,11 @@ typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype_t;
 typedef enum {
   FLCE_CHUNKED = 0,           /* token chunks; one [C,V] buffer overwritten in place by dlogits */
   FLCE_FUSED = 1              /* two passes, no logits buffer: pass 1 per-token log-sum-exp; pass 2
-                                 recomputes each logits tile, keeps its dlogits on chip and adds the
-                                 dx / dW partials into fp32 accumulators with atomics.  bf16 inputs
+                                 recomputes the logits tile by tile, turns them into dlogits and
+                                 adds the dx / dW contributions straight into fp32 accumulators
+                                 with atomics.  Each workgroup holds the dlogits of one block of
+                                 1024 tokens x 1024 vocabulary ids at a time in its own 2 MiB
+                                 buffer (at most 256 of them: 512 MiB of workspace).  bf16 inputs
                                  only.  With bf16 dW the accumulator is an extra V*H*4 bytes; with
                                  fp32 dW it is dW itself.  Results are not bitwise repeatable.
                                  Size limit: (V + 256) * H * 4 and (chunk + 256) * H * 4 below

@@ -40,6 +40,8 @@ struct Plan {
   int64_t k_per_split = 0;
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
+  size_t off_gbuf = 0;                   // fused variant: the workgroups' dlogits block buffers
+  int fused_grid = 0;                    // fused variant: resident workgroups of pass 2
   size_t off_scale = 0;                  // flce::Scale of the call
   size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
   bool fused = false;
@@ -240,6 +242,12 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (p.fused && grads && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
   p.off_dwacc = off;
   if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
+  p.off_gbuf = off;
+  if (p.fused && grads) {   // one dlogits block buffer per resident workgroup of pass 2
+    const int64_t blocks = cdiv(cdiv(p.C, kTile), flce::kFusedBlkM) * cdiv(p.tiles_v, flce::kFusedBlkN);
+    p.fused_grid = (int)std::min<int64_t>(blocks, flce::kFusedMaxGrid);
+    off = align_up(off + (size_t)p.fused_grid * (size_t)flce::kFusedGBlockBytes);
+  }
   if (rms) {   // the chunk's normalised rows, their fp32 dL/dx, rstd, dgamma partials and sum
     p.off_xc = off;    off = align_up(off + (size_t)p.C * H * in_size(cfg));
     p.off_dxc = off;   if (grads) off = align_up(off + (size_t)p.C * H * sizeof(float));
@@ -666,24 +674,26 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
       FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
     }
 
-    flce::FusedArgs fa{};
+    flce::FusedBlockArgs fa{};
     fa.x = xs;
     fa.W = W;
     fa.t = t + s;
     fa.lse = lse + s;
     fa.dx_acc = dx_acc;
     fa.dw_acc = dw_acc;
+    fa.gbuf = ws + p.off_gbuf;
     fa.rows = rows;
     fa.H = (int)p.H;
     fa.V = (int)p.V;
-    fa.tiles_m = tiles_m;
-    fa.tiles_n = p.tiles_v;
     fa.tiles_h = p.tiles_h;
+    fa.blocks_m = (int)cdiv(tiles_m, flce::kFusedBlkM);
+    fa.blocks_n = (int)cdiv(p.tiles_v, flce::kFusedBlkN);
     fa.ign = o.ign;
     fa.scale = scale;
+    const int grid = (int)std::min<int64_t>((int64_t)fa.blocks_m * fa.blocks_n, p.fused_grid);
     // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
     FLCE_LAUNCH(mark(e, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
-    FLCE_LAUNCH(flce::launch_fused_bwd(fa, st));
+    FLCE_LAUNCH(flce::launch_fused_block(fa, grid, st));
     if (!dx32) {
       flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
       FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * rows * p.H, st));

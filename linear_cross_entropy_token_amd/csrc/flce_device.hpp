@@ -154,22 +154,22 @@ struct Operand {
   }
 
   // Copies the slice starting at contraction index k0 (k < k_end valid) into lds_op.
-  // Offsets are 32-bit: every valid byte of the buffer lies below 2^32.
-  __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave) const {
+  // Offsets are 32-bit: every valid byte of the buffer lies below 2^32.  `lane`: the calling
+  // lane (0..63), passed in so that callers decide where lane-dependent values are formed.
+  __device__ __forceinline__ void issue(char* lds_op, int k0, int k_end, int wave, int lane) const {
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) issue_block(lds_op, k0, k_end, wave * BPW + i);
+    for (int i = 0; i < BPW; ++i) issue_block(lds_op, k0, k_end, wave * BPW + i, lane);
   }
 
   // Blocks vw * N .. vw * N + N - 1 of the slice (one wave of a group of 4 copying the whole slice).
   template <int N>
-  __device__ __forceinline__ void issue_part(char* lds_op, int k0, int k_end, int vw) const {
+  __device__ __forceinline__ void issue_part(char* lds_op, int k0, int k_end, int vw, int lane) const {
 #pragma unroll
-    for (int i = 0; i < N; ++i) issue_block(lds_op, k0, k_end, vw * N + i);
+    for (int i = 0; i < N; ++i) issue_block(lds_op, k0, k_end, vw * N + i, lane);
   }
 
   // 1 KiB block b (0 .. 8 BPW - 1) of the slice at k0.
-  __device__ __forceinline__ void issue_block(char* lds_op, int k0, int k_end, int b) const {
-    const int lane = threadIdx.x & 63;
+  __device__ __forceinline__ void issue_block(char* lds_op, int k0, int k_end, int b, int lane) const {
     {
       int mn, kpos;
       uint32_t off;
@@ -288,12 +288,17 @@ __device__ __forceinline__ void lgkm_wait() {
 // 0-3 copy their share after reading slice kt, waves 4-7 before multiplying slice kt-1, and
 // every wave waits for its copies at the end of phase 2kt+1.  There are 2 nk + 1 phases per
 // tile.
-template <typename T, class OpC, class OpR>
+//
+// SWAP exchanges the MFMA's A and B inputs (the row operand becomes A): register rg of block
+// (i, j) in lane l then holds
+//   row = 32 j + 8 (rg / 4) + 4 (l / 32) + rg % 4,   col = 32 i + l % 32,
+// so the 32 lanes of a half-wave hold 32 consecutive columns of one row (the layout for
+// epilogues that issue one atomic per element: each instruction touches two cache lines).
+template <typename T, class OpC, class OpR, bool SWAP = false>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C, const OpR& R,
-                                          int k_begin, int k_end) {
+                                          int k_begin, int k_end, int tid) {
   static_assert(kStages == 2 && kWaves == 8, "the ping-pong schedule pairs the waves of a SIMD over two stages");
   constexpr int BK = slice_k<T>();
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar address arithmetic
   const int rowb = (wave / kWaveCols) * 128;
@@ -308,8 +313,8 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
   auto issue = [&](int kt) {
     char* st = smem + (kt % kStages) * kStageBytes;
     const int k0 = k_begin + kt * BK;
-    C.issue(st, k0, k_end, wave);
-    R.issue(st + kOpBytes, k0, k_end, wave);
+    C.issue(st, k0, k_end, wave, lane);
+    R.issue(st + kOpBytes, k0, k_end, wave, lane);
   };
   u32x4 fa[kSteps][kColBlocks], fb[kSteps][4];
   auto read = [&](int kt) {
@@ -328,7 +333,8 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[kColBlocks][4], char* sm
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = SWAP ? mfma<T>(fb[s][j], fa[s][i], acc[i][j]) : mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
   };
   if (nk > 0) issue(0);
   phase_barrier<true, false>();                 // slice 0 resident
@@ -378,12 +384,11 @@ __device__ __forceinline__ void vm_barrier_keep8(bool keep8) {
 // Measured against gemm_tile at the Llama-3 chunk: logits -11%, dx -3%; dW (both operands
 // read with transposing reads, so its read phases are the longest) stays on gemm_tile.
 constexpr int kDeepRingBytes = 5 * kOpBytes;   // 160 KiB
-template <typename T, class OpC, class OpR>
+template <typename T, class OpC, class OpR, bool SWAP = false>
 __device__ __forceinline__ void gemm_tile_balanced(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C,
-                                                   const OpR& R, int k_begin, int k_end) {
+                                                   const OpR& R, int k_begin, int k_end, int tid) {
   static_assert(kWaves == 8 && kBlocksPerWave == 4, "two groups of 4 waves; 8 blocks per wave copy a slice");
   constexpr int BK = slice_k<T>();
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int vw = wave & 3;                       // position inside the wave group
@@ -417,84 +422,35 @@ __device__ __forceinline__ void gemm_tile_balanced(f32x16 (&acc)[kColBlocks][4],
 #pragma unroll
       for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = SWAP ? mfma<T>(fb[s][j], fa[s][i], acc[i][j]) : mfma<T>(fa[s][i], fb[s][j], acc[i][j]);
   };
   if (nk > 0) {                                  // slice 0: every wave copies its share
-    C.issue(slot_c(0), k_begin, k_end, wave);
-    R.issue(slot_r(0), k_begin, k_end, wave);
+    C.issue(slot_c(0), k_begin, k_end, wave, lane);
+    R.issue(slot_r(0), k_begin, k_end, wave, lane);
   }
   if (wave < kWaves / 2) {
     vm_barrier_keep8(false);                     // slice 0 resident
     for (int m = 0; m < nk; ++m) {
       read(m);                                   // phase 2m
       lgkm_wait();
-      if (m + 1 < nk) R.template issue_part<8>(slot_r(m + 1), k_begin + (m + 1) * BK, k_end, vw);
+      if (m + 1 < nk) R.template issue_part<8>(slot_r(m + 1), k_begin + (m + 1) * BK, k_end, vw, lane);
       phase_barrier<false, false>();
       multiply();                                // phase 2m + 1
       vm_barrier_keep8(false);                   // R(m+1) resident
     }
     phase_barrier<false, false>();               // phase 2nk
   } else {
-    if (1 < nk) C.template issue_part<8>(slot_c(1), k_begin + BK, k_end, vw);
+    if (1 < nk) C.template issue_part<8>(slot_c(1), k_begin + BK, k_end, vw, lane);
     vm_barrier_keep8(1 < nk);                    // slice 0 resident; C(1) may be in flight
     phase_barrier<false, false>();               // phase 0
     for (int m = 0; m < nk; ++m) {
       read(m);                                   // phase 2m + 1
       lgkm_wait();
-      if (m + 2 < nk) C.template issue_part<8>(slot_c(m + 2), k_begin + (m + 2) * BK, k_end, vw);
+      if (m + 2 < nk) C.template issue_part<8>(slot_c(m + 2), k_begin + (m + 2) * BK, k_end, vw, lane);
       vm_barrier_keep8(m + 2 < nk);              // C(m+1) resident
       multiply();                                // phase 2m + 2
       phase_barrier<false, false>();
-    }
-  }
-  __syncthreads();   // LDS free for the epilogue
-}
-
-// The same product with both waves of a SIMD running the same interleaved stream of LDS reads
-// and MFMAs (one k-step's fragments live at a time: 24 registers instead of 96).  For kernels
-// whose other live state leaves no room for the ping-pong schedule's fragment registers.
-template <typename T, class OpC, class OpR>
-__device__ __forceinline__ void gemm_tile_interleaved(f32x16 (&acc)[kColBlocks][4], char* smem, const OpC& C,
-                                                      const OpR& R, int k_begin, int k_end) {
-  static_assert(kStages == 2, "one slice in flight while the other is consumed");
-  constexpr int BK = slice_k<T>();
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int rowb = (wave / kWaveCols) * 128;
-  const int colb = (wave % kWaveCols) * (kTile / kWaveCols);
-#pragma unroll
-  for (int i = 0; i < kColBlocks; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-  if (nk > 0) {
-    C.issue(smem, k_begin, k_end, wave);
-    R.issue(smem + kOpBytes, k_begin, k_end, wave);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt landed (this wave's copies, then the barrier for everyone's); slice kt-1 consumed
-    phase_barrier<true, false>();
-    if (kt + 1 < nk) {
-      char* st = smem + ((kt + 1) % kStages) * kStageBytes;
-      const int k0 = k_begin + (kt + 1) * BK;
-      C.issue(st, k0, k_end, wave);
-      R.issue(st + kOpBytes, k0, k_end, wave);
-    }
-    const char* st = smem + (kt % kStages) * kStageBytes;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      u32x4 a[kColBlocks], b[4];
-#pragma unroll
-      for (int i = 0; i < kColBlocks; ++i) a[i] = read_frag<T, OpC::kKMajor>(st, colb + 32 * i, s, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = read_frag<T, OpR::kKMajor>(st + kOpBytes, rowb + 32 * j, s, lane);
-#pragma unroll
-      for (int i = 0; i < kColBlocks; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma<T>(a[i], b[j], acc[i][j]);
     }
   }
   __syncthreads();   // LDS free for the epilogue
@@ -507,10 +463,19 @@ struct Frag {
   __device__ __forceinline__ int row(int j) const { return rowb + 32 * j + (lane & 31); }
   __device__ __forceinline__ int col0(int i, int q) const { return colb + 32 * i + 8 * q + 4 * (lane >> 5); }
 };
-__device__ __forceinline__ Frag frag_coords() {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ Frag frag_coords(int tid) {
   const int wave = tid >> 6;
   return Frag{(wave / kWaveCols) * 128, (wave % kWaveCols) * (kTile / kWaveCols), tid & 63};
+}
+__device__ __forceinline__ Frag frag_coords() { return frag_coords(threadIdx.x); }
+
+// The thread's id through an empty asm statement: values derived from it are formed where this is
+// called and cannot be hoisted above it (kernels that run several tile products in a loop use it
+// so that each product's lane-dependent addresses stay out of the registers of the others).
+__device__ __forceinline__ int opaque_tid() {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  return tid;
 }
 
 // Logical tile L -> (tm, tn): tiles walk m fastest inside groups of gm m-tiles that sweep

@@ -120,17 +120,26 @@ struct FinalizeArgs {
   const Scale* scale;   // loss = sum / scale->denom
 };
 
-// Fused variant, pass 2: per (token tile, vocabulary tile) the logits tile is recomputed,
-// turned into dlogits in LDS, and fed straight into dx and dW updates (fp32 atomics).
-struct FusedArgs {
+// Fused variant, pass 2: a workgroup owns a block of kFusedBlkM x kFusedBlkN tiles of
+// (tokens x vocabulary); it recomputes their logits once, keeps the block's dlogits in its own
+// bf16 buffer in the workspace, then, per 256-wide slice of H, forms whole dx and dW tiles over
+// the block (contractions of 1024) and adds each with one fp32 atomic per element.
+constexpr int kFusedBlkM = 4;                               // token tiles per block
+constexpr int kFusedBlkN = 4;                               // vocabulary tiles per block
+constexpr int64_t kFusedGBlockBytes = (int64_t)kFusedBlkM * kTileM * kFusedBlkN * kTileN * 2;   // 2 MiB
+constexpr int kFusedMaxGrid = 256;                          // resident workgroups (one per compute unit)
+
+struct FusedBlockArgs {
   const void* x;        // chunk's first token row [rows][H] (bf16)
   const void* W;        // [V][H] (bf16)
   const int64_t* t;     // chunk's targets [rows]
   const float* lse;     // chunk's per-row log-sum-exp [rows]
   float* dx_acc;        // fp32 [rows][H], zeroed before the launch
   float* dw_acc;        // fp32 [V][H], zeroed before the first chunk
+  char* gbuf;           // [gridDim.x][kFusedGBlockBytes]: each workgroup's dlogits block (bf16)
   int rows, H, V;
-  int tiles_m, tiles_n, tiles_h;
+  int tiles_h;
+  int blocks_m, blocks_n;   // token blocks of the chunk, vocabulary blocks
   Ignore ign;
   const Scale* scale;
 };
@@ -185,7 +194,7 @@ hipError_t launch_dx(In in, const DxArgs& a, hipStream_t s);
 hipError_t launch_dx_reduce(const DxReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(In in, const DwArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
-hipError_t launch_fused_bwd(const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused_block(const FusedBlockArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_zero(const FillArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_lse_kernel(LogitsArgs a) {
     rel = (d >= 0 && d < kTile) ? (int)d : -1;
   }
   f32x16 acc[kColBlocks][4];
-  gemm_tile_balanced<T>(acc, smem, C, R, 0, a.H);
+  gemm_tile_balanced<T>(acc, smem, C, R, 0, a.H, threadIdx.x);
 
   const Frag f = frag_coords();
   // [2][kWaveCols][kTile]: per column-wave max, then sum; then the target column per row.  The
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void dx_kernel(DxArgs a) {
   C.init(static_cast<const T*>(a.W), a.H, n0, a.H, (uint32_t)((int64_t)a.V * a.H * ES));
   R.init(static_cast<const T*>(a.g), a.ldg, m0, a.rows, (uint32_t)((int64_t)a.rows * a.ldg * ES));
   f32x16 acc[kColBlocks][4];
-  gemm_tile_balanced<T>(acc, smem, C, R, ks, ke);
+  gemm_tile_balanced<T>(acc, smem, C, R, ks, ke, threadIdx.x);
 
   const Frag f = frag_coords();
 #pragma unroll
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_kernel(DwArgs a) {
   C.init(static_cast<const T*>(a.x), a.H, n0, a.H, (uint32_t)((int64_t)a.rows * a.H * ES));
   R.init(static_cast<const T*>(a.g), a.ldg, m0, (int)a.ldg, (uint32_t)((int64_t)a.rows * a.ldg * ES));
   f32x16 acc[kColBlocks][4];
-  gemm_tile<T>(acc, smem, C, R, 0, a.rows);
+  gemm_tile<T>(acc, smem, C, R, 0, a.rows, threadIdx.x);
 
   const Frag f = frag_coords();
   if (a.dw_fp32) {
