@@ -223,13 +223,23 @@ def fused_record(flce, x, W, t, w, chunk, steps, ignore, reduction):
             k["tflops_executed"] = round(st["flops"] / st["launches"] / (avg * 1e-3) / 1e12, 1)
         kernels[name] = k
     log(f"[bench] fused: {ms:.2f} ms/step, loss {lval:.6f}")
+    fb = stats.get("fused_bwd")
+    roof = None
+    if fb and fb["launches"] > 0:
+        avg_s = fb["total_ms"] / fb["launches"] * 1e-3
+        ach = fb["flops"] / fb["launches"] / avg_s / 1e12      # executed: recompute + dx + dW products
+        eff_chunk = flce.flce_effective_chunk(w.N, w.H, w.V, chunk)
+        roof = {"bound": "mfma", "kernel": "fused_bwd", "achieved": round(ach, 1), "peak": PEAK_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS["bf16"], 4),
+                "traffic": measured_traffic("fused_bwd", w.name, eff_chunk),
+                "flops_per_launch": fb["flops"] / fb["launches"], "avg_launch_ms": round(avg_s * 1e3, 4)}
     return {"variant": "fused", "grad_dtype": "fp32", "steps": steps, "warmup": 1, "ms_per_step": round(ms, 4),
             "tokens_per_s": round(w.N / (ms * 1e-3), 1),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
             "mfma_peak_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
             "tflops_executed": round(8.0 / 6.0 * fl / (ms * 1e-3) / 1e12, 1),
             "peak_extra_gb": round(peak_extra / 1e9, 3), "workspace_gb": round(ws / 1e9, 3),
-            "loss": round(lval, 6), "kernels": kernels}
+            "loss": round(lval, 6), "kernels": kernels, "roofline": roof}
 
 
 def main():
