@@ -75,8 +75,11 @@ typedef enum {
                                  recomputes the logits tile by tile, turns them into dlogits and
                                  adds the dx / dW contributions straight into fp32 accumulators
                                  with atomics.  Each workgroup holds the dlogits of one block of
-                                 1024 tokens x 1024 vocabulary ids at a time in its own 2 MiB
-                                 buffer (at most 256 of them: 512 MiB of workspace).  bf16 inputs
+                                 at most 2048 tokens x 1024 vocabulary ids at a time in its own
+                                 4 MiB buffer (at most 256 of them: 1 GiB of workspace).  With fp32
+                                 dx, pass 2 runs once over all N tokens after every chunk's pass 1
+                                 (dx is its own accumulator); with bf16 dx, once per chunk into an
+                                 fp32 [chunk, H] accumulator.  bf16 inputs
                                  only.  With bf16 dW the accumulator is an extra V*H*4 bytes; with
                                  fp32 dW it is dW itself.  Results are not bitwise repeatable.
                                  Size limit: (V + 256) * H * 4 and (chunk + 256) * H * 4 below

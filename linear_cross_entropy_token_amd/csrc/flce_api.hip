@@ -42,6 +42,7 @@ struct Plan {
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
   size_t off_gbuf = 0;                   // fused variant: the workgroups' dlogits block buffers
   int fused_grid = 0;                    // fused variant: resident workgroups of pass 2
+  bool fused_all = false;                // fused variant: one pass 2 over all N (fp32 dx) instead of per chunk
   size_t off_scale = 0;                  // flce::Scale of the call
   size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
   bool fused = false;
@@ -204,6 +205,26 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
+// Block shape of a fused pass-2 launch over tm token tiles and tv vocabulary tiles: the largest of
+// flce::kFusedShapes whose blocks fill the resident workgroups' rounds to at least 85%, else the
+// smallest (fewer atomics per element for larger blocks; enough blocks for the compute units).
+void fused_shape(int64_t tm, int64_t tv, int& bm, int& bn) {
+  for (const auto& sh : flce::kFusedShapes) {
+    bm = sh[0];
+    bn = sh[1];
+    const int64_t nb = cdiv(tm, bm) * cdiv(tv, bn);
+    const int64_t rounds = cdiv(nb, flce::kFusedMaxGrid);
+    if ((double)nb >= 0.85 * (double)(rounds * flce::kFusedMaxGrid)) return;
+  }
+}
+
+// Whether the fused variant runs pass 2 once over all N tokens: dx in fp32 (dx is its own
+// accumulator) and N rows of x and of dx within the kernels' 32-bit buffer offsets.
+bool fused_pass2_over_all(const flce_config_t& cfg, int64_t N, int64_t H) {
+  const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
+  return cfg.dx_dtype == FLCE_FP32 && N * H * 2 < lim && (N + kTile) * H * 4 < lim;
+}
+
 Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true,
                bool rms = false) {
   Plan p;
@@ -244,7 +265,11 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
   p.off_gbuf = off;
   if (p.fused && grads) {   // one dlogits block buffer per resident workgroup of pass 2
-    const int64_t blocks = cdiv(cdiv(p.C, kTile), flce::kFusedBlkM) * cdiv(p.tiles_v, flce::kFusedBlkN);
+    p.fused_all = fused_pass2_over_all(cfg, N, H);
+    const int64_t rows = p.fused_all ? N : p.C;
+    int bm = 0, bn = 0;
+    fused_shape(cdiv(rows, kTile), p.tiles_v, bm, bn);
+    const int64_t blocks = cdiv(cdiv(rows, kTile), bm) * cdiv(p.tiles_v, bn);
     p.fused_grid = (int)std::min<int64_t>(blocks, flce::kFusedMaxGrid);
     off = align_up(off + (size_t)p.fused_grid * (size_t)flce::kFusedGBlockBytes);
   }
@@ -603,6 +628,41 @@ flce_status_t run_rmsnorm(const Exec& e, const Plan& p, const Opts& o, const voi
 
 // Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and pass 2
 // (recompute, dlogits in LDS, dx and dW partials by fp32 atomics); outputs converted last.
+// Pass 2 of the fused variant over `rows` tokens starting at token s: dlogits recomputed block by
+// block and added into dx_acc (rows x H, fp32) and dw_acc (V x H, fp32).
+flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t s, int64_t rows, const void* x,
+                           const void* W, const int64_t* t, const float* lse, float* dx_acc, float* dw_acc,
+                           hipStream_t st) {
+  const double VH = (double)p.V * (double)p.H;
+  flce::FusedBlockArgs fa{};
+  fa.x = static_cast<const char*>(x) + (size_t)s * p.H * 2;
+  fa.W = W;
+  fa.t = t + s;
+  fa.lse = lse + s;
+  fa.dx_acc = dx_acc;
+  fa.dw_acc = dw_acc;
+  fa.gbuf = e.ws + p.off_gbuf;
+  fa.rows = (int)rows;
+  fa.H = (int)p.H;
+  fa.V = (int)p.V;
+  fa.tiles_h = p.tiles_h;
+  fused_shape(cdiv(rows, kTile), p.tiles_v, fa.bm, fa.bn);
+  fa.blocks_m = (int)cdiv(cdiv(rows, kTile), fa.bm);
+  fa.blocks_n = (int)cdiv(p.tiles_v, fa.bn);
+  fa.group_m = std::max(1, 16 / fa.bm);   // token blocks per 4096 tokens
+  fa.ign = o.ign;
+  fa.scale = reinterpret_cast<const flce::Scale*>(e.ws + p.off_scale);
+  const int grid = (int)std::min<int64_t>((int64_t)fa.blocks_m * fa.blocks_n, p.fused_grid);
+  // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
+  FLCE_LAUNCH(mark(e, K_FUSED_BWD, 6.0 * (double)rows * VH, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
+  FLCE_LAUNCH(flce::launch_fused_block(fa, grid, st));
+  return FLCE_OK;
+}
+
+// Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and the combine into
+// each token's lse; pass 2 (recompute, dlogits per block, dx and dW by fp32 atomics) once over all
+// tokens when dx is fp32 (dx is then its own accumulator, and one launch has the most blocks),
+// else per chunk into an fp32 chunk accumulator cast to bf16 after it; outputs converted last.
 flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void* x, const void* W,
                         const int64_t* t, float* loss, void* dx, void* dW, float* lse_out, hipStream_t st) {
   const flce_config_t& cfg = e.h->cfg;
@@ -625,14 +685,18 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
     FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * VH, st));
     FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
   }
+  if (o.grads && p.fused_all && !o.accumulate) {
+    flce::FillArgs zx{static_cast<float*>(dx), p.N * p.H};
+    FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * (double)p.N * p.H, st));
+    FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
+  }
   for (int64_t s = 0; s < p.N; s += p.C) {
     const int rows = (int)std::min(p.C, p.N - s);
     const int tiles_m = (int)cdiv(rows, kTile);
     const double gemm_flops = 2.0 * rows * VH;
-    const void* xs = static_cast<const char*>(x) + (size_t)s * p.H * 2;
 
     flce::LogitsArgs la{};
-    la.x = xs;
+    la.x = static_cast<const char*>(x) + (size_t)s * p.H * 2;
     la.W = W;
     la.t = t + s;
     la.z = nullptr;
@@ -665,7 +729,7 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
     ca.V = (int)p.V;
     FLCE_LAUNCH(mark(e, K_COMBINE, 0.0, 8.0 * rows * p.tiles_v + 16.0 * rows, st));
     FLCE_LAUNCH(flce::launch_combine(ca, st));
-    if (!o.grads) continue;
+    if (!o.grads || p.fused_all) continue;
 
     float* dx_acc = dx32 ? static_cast<float*>(dx) + (size_t)s * p.H : reinterpret_cast<float*>(ws + p.off_dxacc);
     if (!(dx32 && o.accumulate)) {
@@ -673,32 +737,17 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
       FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
     }
-
-    flce::FusedBlockArgs fa{};
-    fa.x = xs;
-    fa.W = W;
-    fa.t = t + s;
-    fa.lse = lse + s;
-    fa.dx_acc = dx_acc;
-    fa.dw_acc = dw_acc;
-    fa.gbuf = ws + p.off_gbuf;
-    fa.rows = rows;
-    fa.H = (int)p.H;
-    fa.V = (int)p.V;
-    fa.tiles_h = p.tiles_h;
-    fa.blocks_m = (int)cdiv(tiles_m, flce::kFusedBlkM);
-    fa.blocks_n = (int)cdiv(p.tiles_v, flce::kFusedBlkN);
-    fa.ign = o.ign;
-    fa.scale = scale;
-    const int grid = (int)std::min<int64_t>((int64_t)fa.blocks_m * fa.blocks_n, p.fused_grid);
-    // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
-    FLCE_LAUNCH(mark(e, K_FUSED_BWD, 3.0 * gemm_flops, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
-    FLCE_LAUNCH(flce::launch_fused_block(fa, grid, st));
+    const flce_status_t r = launch_pass2(e, p, o, s, rows, x, W, t, lse, dx_acc, dw_acc, st);
+    if (r != FLCE_OK) return r;
     if (!dx32) {
       flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
       FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_cast_bf16(cx, st));
     }
+  }
+  if (o.grads && p.fused_all) {
+    const flce_status_t r = launch_pass2(e, p, o, 0, p.N, x, W, t, lse, static_cast<float*>(dx), dw_acc, st);
+    if (r != FLCE_OK) return r;
   }
   if (o.grads && !dw32) {
     flce::CastArgs cw{dw_acc, dW, p.V * p.H, o.accumulate};

@@ -16,23 +16,25 @@ namespace flce {
 // Pass 2.  Each add of a 256 x 256 partial tile into dx or dW costs one fp32 atomic per element;
 // a kernel that added one partial per (token tile, vocabulary tile) pair would make 2 rows V H /
 // 256 adds per chunk (16.8 G at 4096 tokens, V = 128,256, H = 4,096: bound by the L2's atomic
-// rate).  Here a workgroup owns a block of kFusedBlkM x kFusedBlkN tile pairs (1024 tokens x
-// 1024 vocabulary ids):
-//   A. it recomputes the block's 16 logits tiles (contraction over H on the tile engine), turns
+// rate).  Here a workgroup owns a block of BM x BN tile pairs (at most 8 x 4: 2048 tokens x 1024
+// vocabulary ids):
+//   A. it recomputes the block's BM x BN logits tiles (contraction over H on the tile engine), turns
 //      each into dlogits G = (exp(z - lse) - onehot) * scale and stores it, bf16, in its own
-//      2 MiB block buffer in the workspace (the dlogits tile of the FLCE page's step 2, now for
+//      block buffer (4 MiB) in the workspace (the dlogits tile of the FLCE page's step 2, now for
 //      a block of tiles; it never leaves the workspace and is overwritten by the next block);
-//   B. for each 256-wide slice of H it forms the block's 4 dx tiles (G rows times W, contraction
-//      over the block's 1024 vocabulary ids) and 4 dW tiles (G columns times x, contraction over
-//      its 1024 tokens) on the same engine and adds each into the fp32 accumulators with
+//   B. for each 256-wide slice of H it forms the block's BM dx tiles (G rows times W, contraction
+//      over the block's 256 BN vocabulary ids) and BN dW tiles (G columns times x, contraction
+//      over its 256 BM tokens) on the same engine and adds each into the fp32 accumulators with
 //      atomics (the reduction by atomic adds of the "Unsloth deep architecture" page's streaming
 //      CE kernel).
-// So every dx / dW element receives one atomic per vocabulary block / token block: 4 x fewer.
+// So every dx / dW element receives one atomic per vocabulary block / token block: BN x / BM x
+// fewer than with one atomic per tile pair (3.2 G adds instead of 16.8 G at the Llama-3 chunk
+// with 8 x 4).
 // The grid is persistent (at most one workgroup per compute unit), each workgroup walking blocks
-// L, L + grid, ...; the buffer a workgroup writes is read back only by itself
+// L, L + grid, ... in groups of token blocks that sweep the whole vocabulary (4096 tokens per
+// group: a round of workgroups then shares the group's rows of x and of the dx accumulator); the buffer a workgroup writes is read back only by itself
 // (program order plus a barrier: the writes are complete before any wave reads).
 // ---------------------------------------------------------------------------
-constexpr int kGLd = kFusedBlkN * kTile;   // bf16 elements per row of a dlogits block
 
 // Adds a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c] with
 // one atomic per element; rows >= row_end and columns >= H are skipped.
@@ -61,7 +63,9 @@ __device__ __forceinline__ void atomic_add_tile(const f32x16 (&acc)[kColBlocks][
   }
 }
 
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs a) {
+  constexpr int kGLd = BN * kTile;   // bf16 elements per row of a dlogits block
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -74,10 +78,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs
   // stay live across every product (each needs nearly all of the register file).
 
   for (int blk = L; blk < nblocks; blk += gridDim.x) {
-    const int tok0 = (blk % a.blocks_m) * kFusedBlkM * kTile;   // first token of the block (chunk-relative)
-    const int voc0 = (blk / a.blocks_m) * kFusedBlkN * kTile;   // first vocabulary id of the block
-    const int ntok = min(kFusedBlkM * kTile, a.rows - tok0);    // valid tokens / ids of the block
-    const int nvoc = min(kFusedBlkN * kTile, a.V - voc0);
+    int bmi, bni;
+    grouped_tile(blk, a.blocks_m, a.blocks_n, a.group_m, bmi, bni);
+    const int tok0 = bmi * BM * kTile;   // first token of the block (launch-relative)
+    const int voc0 = bni * BN * kTile;   // first vocabulary id of the block
+    const int ntok = min(BM * kTile, a.rows - tok0);    // valid tokens / ids of the block
+    const int nvoc = min(BN * kTile, a.V - voc0);
 
     // A. dlogits of the block's tiles into its buffer
     for (int mi = 0; mi * kTile < ntok; ++mi) {
@@ -197,7 +203,12 @@ static inline int grid_for(int64_t n4) {
 }
 
 hipError_t launch_fused_block(const FusedBlockArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(fused_block_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  const int shape = a.bm * 16 + a.bn;
+  if (shape == 8 * 16 + 4) hipLaunchKernelGGL((fused_block_kernel<8, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (shape == 4 * 16 + 4) hipLaunchKernelGGL((fused_block_kernel<4, 4>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (shape == 4 * 16 + 2) hipLaunchKernelGGL((fused_block_kernel<4, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else if (shape == 2 * 16 + 2) hipLaunchKernelGGL((fused_block_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

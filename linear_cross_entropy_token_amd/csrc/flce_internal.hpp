@@ -120,26 +120,30 @@ struct FinalizeArgs {
   const Scale* scale;   // loss = sum / scale->denom
 };
 
-// Fused variant, pass 2: a workgroup owns a block of kFusedBlkM x kFusedBlkN tiles of
-// (tokens x vocabulary); it recomputes their logits once, keeps the block's dlogits in its own
-// bf16 buffer in the workspace, then, per 256-wide slice of H, forms whole dx and dW tiles over
-// the block (contractions of 1024) and adds each with one fp32 atomic per element.
-constexpr int kFusedBlkM = 4;                               // token tiles per block
-constexpr int kFusedBlkN = 4;                               // vocabulary tiles per block
-constexpr int64_t kFusedGBlockBytes = (int64_t)kFusedBlkM * kTileM * kFusedBlkN * kTileN * 2;   // 2 MiB
+// Fused variant, pass 2: a workgroup owns a block of bm x bn tiles of (tokens x vocabulary); it
+// recomputes their logits once, keeps the block's dlogits in its own bf16 buffer in the workspace,
+// then, per 256-wide slice of H, forms whole dx and dW tiles over the block and adds each with one
+// fp32 atomic per element.  The atomic count, rows V H (1 / (256 bn) + 1 / (256 bm)), sets the
+// time (measured at the Llama-3 chunk, fused_bwd per 4096 tokens: 2 x 2 tiles 32.8 ms, 4 x 4 19.2,
+// 4 x 8 18.0, 8 x 4 17.1), so the largest block is best as long as there are enough blocks to keep
+// every compute unit busy.  The shapes the kernel is built for, largest first:
+constexpr int kFusedShapes[4][2] = {{8, 4}, {4, 4}, {4, 2}, {2, 2}};
+constexpr int64_t kFusedGBlockBytes = (int64_t)8 * kTileM * 4 * kTileN * 2;   // 4 MiB: the largest shape's buffer
 constexpr int kFusedMaxGrid = 256;                          // resident workgroups (one per compute unit)
 
 struct FusedBlockArgs {
-  const void* x;        // chunk's first token row [rows][H] (bf16)
+  const void* x;        // first token row of the launch [rows][H] (bf16)
   const void* W;        // [V][H] (bf16)
-  const int64_t* t;     // chunk's targets [rows]
-  const float* lse;     // chunk's per-row log-sum-exp [rows]
-  float* dx_acc;        // fp32 [rows][H], zeroed before the launch
-  float* dw_acc;        // fp32 [V][H], zeroed before the first chunk
+  const int64_t* t;     // targets of those rows [rows]
+  const float* lse;     // their log-sum-exp [rows]
+  float* dx_acc;        // fp32 [rows][H], cleared (or holding the values to add to) before the launch
+  float* dw_acc;        // fp32 [V][H], cleared before the first launch of a call
   char* gbuf;           // [gridDim.x][kFusedGBlockBytes]: each workgroup's dlogits block (bf16)
   int rows, H, V;
   int tiles_h;
-  int blocks_m, blocks_n;   // token blocks of the chunk, vocabulary blocks
+  int bm, bn;               // block shape in tiles: one of kFusedShapes
+  int blocks_m, blocks_n;   // token blocks of the launch, vocabulary blocks
+  int group_m;              // blocks are walked in groups of group_m token blocks that sweep all vocabulary blocks
   Ignore ign;
   const Scale* scale;
 };
