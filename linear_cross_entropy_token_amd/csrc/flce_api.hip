@@ -235,13 +235,17 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.Vp = cdiv(V, kTile) * kTile;
   p.tiles_v = (int)(p.Vp / kTile);
   p.tiles_h = (int)cdiv(H, kTile);
-  // dx = G W has only ceil(C/256) x ceil(H/256) output tiles: split the vocabulary
-  // contraction so that about one workgroup per compute unit (256 CUs) runs.
+  // dx = G W has only ceil(C/256) x ceil(H/256) output tiles: split the vocabulary contraction
+  // into the fewest parts (at most 8, each at least 8 k-slices) whose tiles fill the rounds of
+  // 256 compute units to at least 90% (e.g. 384 tiles, 1.5 rounds, become 768 in 3 rounds).
   const int64_t tiles_dx = cdiv(p.C, kTile) * p.tiles_h;
   const int64_t bk = flce::kSliceBytesABI / (int64_t)in_size(cfg);   // contraction elements per k-slice
-  int64_t s = std::max<int64_t>(1, 256 / tiles_dx);
-  s = std::min<int64_t>(s, 8);
-  s = std::min<int64_t>(s, std::max<int64_t>(1, p.Vp / (8 * bk)));
+  const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(8, p.Vp / (8 * bk)));
+  int64_t s = 1;
+  for (; s < smax; ++s) {
+    const int64_t n = tiles_dx * s;
+    if ((double)n >= 0.9 * (double)(cdiv(n, 256) * 256)) break;
+  }
   p.splits = (int)s;
   p.k_per_split = cdiv(cdiv(p.Vp, s), bk) * bk;
 
