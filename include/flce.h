@@ -74,9 +74,10 @@ typedef enum {
   FLCE_FUSED = 1              /* two passes, no logits buffer: pass 1 per-token log-sum-exp; pass 2
                                  recomputes the logits tile by tile, turns them into dlogits and
                                  adds the dx / dW contributions straight into fp32 accumulators
-                                 with atomics.  Each workgroup holds the dlogits of one block of
-                                 at most 2048 tokens x 1024 vocabulary ids at a time in its own
-                                 4 MiB buffer (at most 256 of them: 1 GiB of workspace).  With fp32
+                                 with atomics.  Each workgroup holds the dlogits of one piece of
+                                 at most 2048 tokens x 1536 vocabulary ids at a time in its own
+                                 buffer of at most 6 MiB (at most 256 of them: 1.5 GiB of
+                                 workspace).  With fp32
                                  dx, pass 2 runs once over all N tokens after every chunk's pass 1
                                  (dx is its own accumulator); with bf16 dx, once per chunk into an
                                  fp32 [chunk, H] accumulator.  bf16 inputs

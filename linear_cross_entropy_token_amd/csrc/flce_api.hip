@@ -42,6 +42,9 @@ struct Plan {
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
   size_t off_gbuf = 0;                   // fused variant: the workgroups' dlogits block buffers
   int fused_grid = 0;                    // fused variant: resident workgroups of pass 2
+  int fused_bm = 0;                      // fused variant: token tiles per row of pass-2 cells
+  int fused_bnmax = 0;                   // fused variant: widest pass-2 piece, in vocabulary tiles
+  bool fused_blocks = false;             // fused variant: pass-2 pieces dealt as blocks (else spans)
   bool fused_all = false;                // fused variant: one pass 2 over all N (fp32 dx) instead of per chunk
   size_t off_scale = 0;                  // flce::Scale of the call
   size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
@@ -205,16 +208,73 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
-// Block shape of a fused pass-2 launch over tm token tiles and tv vocabulary tiles: the largest of
-// flce::kFusedShapes whose blocks fill the resident workgroups' rounds to at least 85%, else the
-// smallest (fewer atomics per element for larger blocks; enough blocks for the compute units).
-void fused_shape(int64_t tm, int64_t tv, int& bm, int& bn) {
-  for (const auto& sh : flce::kFusedShapes) {
-    bm = sh[0];
-    bn = sh[1];
-    const int64_t nb = cdiv(tm, bm) * cdiv(tv, bn);
-    const int64_t rounds = cdiv(nb, flce::kFusedMaxGrid);
-    if ((double)nb >= 0.85 * (double)(rounds * flce::kFusedMaxGrid)) return;
+// Pass-2 work decomposition over tm token tiles and tv vocabulary tiles with rows of bm token tiles,
+// pieces at most bnmax vocabulary tiles wide (blocks: exactly, the last of a row narrower) and at
+// most gmax workgroups.
+flce::SpanPlan span_plan(int64_t tm, int64_t tv, int bm, int bnmax, int gmax, bool blocks) {
+  flce::SpanPlan sp;
+  sp.blocks = blocks ? 1 : 0;
+  sp.R = (int)cdiv(tm, bm);
+  sp.tv = (int)tv;
+  sp.S = flce::span_supers(sp.tv);
+  sp.gm = std::max(1, 16 / bm);   // block groups of 4096 tokens
+  sp.bnmax = bnmax;
+  const int64_t units = blocks ? (int64_t)sp.R * cdiv(tv, bnmax) : (int64_t)sp.R * tv;
+  sp.G = (int)std::min<int64_t>(gmax, units);
+  return sp;
+}
+
+// Relative cost of a pass-2 piece of h x w tiles: h w tile products of each kind against h + w
+// atomic tile adds per 256-wide slice of H, weighted as the measured block shapes give it (per
+// 4096-token chunk at V = 128,256, H = 4,096: 2 x 2 tiles 32.8 ms, 4 x 4 19.2 ms, 8 x 4 17.1 ms fit
+// about 0.18 ms per tile pair and 0.85 ms per atomic tile add and slice of H).
+constexpr double kAtomicWeight = 4.9;
+
+// The slowest workgroup's cost under a decomposition, and its widest piece.
+double span_cost(const flce::SpanPlan& sp, int64_t tm, int bm, int& maxw) {
+  double worst = 0.0;
+  maxw = 0;
+  for (int L = 0; L < sp.G; ++L) {
+    int r = 0, v0 = 0, n = 0;
+    double cost = 0.0;
+    for (int k = 0; flce::span_piece(sp, L, k, r, v0, n); ++k) {
+      const double h = (double)std::min<int64_t>(bm, tm - (int64_t)r * bm);
+      cost += h * n + kAtomicWeight * (h + n);
+      maxw = std::max(maxw, n);
+    }
+    worst = std::max(worst, cost);
+  }
+  return worst;
+}
+
+// Decomposition of the fused pass 2 over tm token tiles and tv vocabulary tiles.  Blocks of 8 x 6 or
+// 8 x 4 tiles (2048 tokens x 1536 / 1024 vocabulary ids) when they fill the rounds of resident
+// workgroups to 99% (measured: where they do, blocks are up to 8% faster than spans with the same
+// pieces); else spans with the row height (8, 4 or 2 token tiles; widest piece 48 / bm tiles, 6 MiB
+// of bf16 dlogits) whose slowest workgroup costs least.  bnmax ends up as the widest piece used.
+void fused_work(int64_t tm, int64_t tv, bool& blocks, int& bm, int& bnmax) {
+  for (const int bn : {6, 4}) {
+    const int64_t nb = cdiv(tm, 8) * cdiv(tv, bn);
+    const int64_t slots = cdiv(nb, flce::kFusedMaxGrid) * flce::kFusedMaxGrid;
+    if (tm % 8 == 0 && (double)nb >= 0.99 * (double)slots) {
+      blocks = true;
+      bm = 8;
+      bnmax = (int)std::min<int64_t>(bn, tv);
+      return;
+    }
+  }
+  blocks = false;
+  double best = 0.0;
+  bm = 0;
+  for (const int h : {8, 4, 2}) {
+    int w = 0;
+    const double c =
+        span_cost(span_plan(tm, tv, h, flce::kFusedPieceTiles / h, flce::kFusedMaxGrid, false), tm, h, w);
+    if (bm == 0 || c < best) {
+      best = c;
+      bm = h;
+      bnmax = w;
+    }
   }
 }
 
@@ -224,6 +284,9 @@ bool fused_pass2_over_all(const flce_config_t& cfg, int64_t N, int64_t H) {
   const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
   return cfg.dx_dtype == FLCE_FP32 && N * H * 2 < lim && (N + kTile) * H * 4 < lim;
 }
+
+// Bytes of one workgroup's pass-2 dlogits piece buffer: bm x 256 rows of bnmax x 256 bf16.
+size_t fused_piece_bytes(const Plan& p) { return (size_t)p.fused_bm * kTile * (size_t)p.fused_bnmax * kTile * 2; }
 
 Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true,
                bool rms = false) {
@@ -271,11 +334,10 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (p.fused && grads) {   // one dlogits block buffer per resident workgroup of pass 2
     p.fused_all = fused_pass2_over_all(cfg, N, H);
     const int64_t rows = p.fused_all ? N : p.C;
-    int bm = 0, bn = 0;
-    fused_shape(cdiv(rows, kTile), p.tiles_v, bm, bn);
-    const int64_t blocks = cdiv(cdiv(rows, kTile), bm) * cdiv(p.tiles_v, bn);
-    p.fused_grid = (int)std::min<int64_t>(blocks, flce::kFusedMaxGrid);
-    off = align_up(off + (size_t)p.fused_grid * (size_t)flce::kFusedGBlockBytes);
+    fused_work(cdiv(rows, kTile), p.tiles_v, p.fused_blocks, p.fused_bm, p.fused_bnmax);
+    p.fused_grid =
+        span_plan(cdiv(rows, kTile), p.tiles_v, p.fused_bm, p.fused_bnmax, flce::kFusedMaxGrid, p.fused_blocks).G;
+    off = align_up(off + (size_t)p.fused_grid * (size_t)fused_piece_bytes(p));
   }
   if (rms) {   // the chunk's normalised rows, their fp32 dL/dx, rstd, dgamma partials and sum
     p.off_xc = off;    off = align_up(off + (size_t)p.C * H * in_size(cfg));
@@ -650,13 +712,15 @@ flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t 
   fa.H = (int)p.H;
   fa.V = (int)p.V;
   fa.tiles_h = p.tiles_h;
-  fused_shape(cdiv(rows, kTile), p.tiles_v, fa.bm, fa.bn);
-  fa.blocks_m = (int)cdiv(cdiv(rows, kTile), fa.bm);
-  fa.blocks_n = (int)cdiv(p.tiles_v, fa.bn);
-  fa.group_m = std::max(1, 16 / fa.bm);   // token blocks per 4096 tokens
+  // the plan's row height and widest piece (its buffers are sized for them); a launch over fewer
+  // tokens than the plan's (the last chunk) only has fewer cells
+  fa.bm = p.fused_bm;
+  fa.span = span_plan(cdiv(rows, kTile), p.tiles_v, p.fused_bm, p.fused_bnmax, p.fused_grid, p.fused_blocks);
+  fa.gld = p.fused_bnmax * kTile;
+  fa.gstride = (int64_t)fused_piece_bytes(p);
   fa.ign = o.ign;
   fa.scale = reinterpret_cast<const flce::Scale*>(e.ws + p.off_scale);
-  const int grid = (int)std::min<int64_t>((int64_t)fa.blocks_m * fa.blocks_n, p.fused_grid);
+  const int grid = fa.span.G;
   // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
   FLCE_LAUNCH(mark(e, K_FUSED_BWD, 6.0 * (double)rows * VH, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
   FLCE_LAUNCH(flce::launch_fused_block(fa, grid, st));

@@ -15,25 +15,21 @@ namespace flce {
 // ---------------------------------------------------------------------------
 // Pass 2.  Each add of a 256 x 256 partial tile into dx or dW costs one fp32 atomic per element;
 // a kernel that added one partial per (token tile, vocabulary tile) pair would make 2 rows V H /
-// 256 adds per chunk (16.8 G at 4096 tokens, V = 128,256, H = 4,096: bound by the L2's atomic
-// rate).  Here a workgroup owns a block of BM x BN tile pairs (at most 8 x 4: 2048 tokens x 1024
-// vocabulary ids):
-//   A. it recomputes the block's BM x BN logits tiles (contraction over H on the tile engine), turns
-//      each into dlogits G = (exp(z - lse) - onehot) * scale and stores it, bf16, in its own
-//      block buffer (4 MiB) in the workspace (the dlogits tile of the FLCE page's step 2, now for
-//      a block of tiles; it never leaves the workspace and is overwritten by the next block);
-//   B. for each 256-wide slice of H it forms the block's BM dx tiles (G rows times W, contraction
-//      over the block's 256 BN vocabulary ids) and BN dW tiles (G columns times x, contraction
-//      over its 256 BM tokens) on the same engine and adds each into the fp32 accumulators with
-//      atomics (the reduction by atomic adds of the "Unsloth deep architecture" page's streaming
-//      CE kernel).
-// So every dx / dW element receives one atomic per vocabulary block / token block: BN x / BM x
-// fewer than with one atomic per tile pair (3.2 G adds instead of 16.8 G at the Llama-3 chunk
-// with 8 x 4).
-// The grid is persistent (at most one workgroup per compute unit), each workgroup walking blocks
-// L, L + grid, ... in groups of token blocks that sweep the whole vocabulary (4096 tokens per
-// group: a round of workgroups then shares the group's rows of x and of the dx accumulator); the buffer a workgroup writes is read back only by itself
-// (program order plus a barrier: the writes are complete before any wave reads).
+// 256 adds per chunk (16.8 G at 4096 tokens, V = 128,256, H = 4,096: bound by the atomics).  Here a
+// workgroup works on pieces of bm x w tile pairs (up to 8 x 6: 2048 tokens x 1536 vocabulary ids):
+//   A. it recomputes the piece's logits tiles (contraction over H on the tile engine), turns each
+//      into dlogits G = (exp(z - lse) - onehot) * scale and stores it, bf16, in its own piece
+//      buffer in the workspace (the dlogits tile of the FLCE page's step 2, now for a block of
+//      tiles; it never leaves the workspace and is overwritten by the next piece);
+//   B. for each 256-wide slice of H it forms the piece's bm dx tiles (G rows times W, contraction
+//      over the piece's vocabulary ids) and w dW tiles (G columns times x, contraction over its
+//      tokens) on the same engine and adds each into the fp32 accumulators with atomics (the
+//      reduction by atomic adds of the "Unsloth deep architecture" page's streaming CE kernel).
+// So every dx / dW element receives one atomic per piece that covers it: w x / bm x fewer than
+// with one atomic per tile pair.  The grid is persistent (at most one workgroup per compute unit);
+// span_piece deals the pieces (flce_internal.hpp).  The buffer a
+// workgroup writes is read back only by itself (program order plus a barrier: the writes are
+// complete before any wave reads).
 // ---------------------------------------------------------------------------
 
 // Adds a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c] with
@@ -63,29 +59,27 @@ __device__ __forceinline__ void atomic_add_tile(const f32x16 (&acc)[kColBlocks][
   }
 }
 
-template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs a) {
-  constexpr int kGLd = BN * kTile;   // bf16 elements per row of a dlogits block
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  bf16_t* G = reinterpret_cast<bf16_t*>(a.gbuf + (int64_t)L * kFusedGBlockBytes);
+  bf16_t* G = reinterpret_cast<bf16_t*>(a.gbuf + (int64_t)L * a.gstride);
   const bf16_t* X = static_cast<const bf16_t*>(a.x);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const int nblocks = a.blocks_m * a.blocks_n;
+  const int gld = a.gld;
+  const uint32_t gbytes = (uint32_t)a.gstride;
   // Every lane-dependent value below is formed from a fresh opaque_tid() next to its use: this
   // kernel runs three kinds of tile product in loops, and values hoisted out of those loops would
   // stay live across every product (each needs nearly all of the register file).
 
-  for (int blk = L; blk < nblocks; blk += gridDim.x) {
-    int bmi, bni;
-    grouped_tile(blk, a.blocks_m, a.blocks_n, a.group_m, bmi, bni);
-    const int tok0 = bmi * BM * kTile;   // first token of the block (launch-relative)
-    const int voc0 = bni * BN * kTile;   // first vocabulary id of the block
-    const int ntok = min(BM * kTile, a.rows - tok0);    // valid tokens / ids of the block
-    const int nvoc = min(BN * kTile, a.V - voc0);
+  int row, vt0, nvt;
+  for (int k = 0; span_piece(a.span, L, k, row, vt0, nvt); ++k) {
+    const int tok0 = row * a.bm * kTile;   // first token of the piece (launch-relative)
+    const int voc0 = vt0 * kTile;          // first vocabulary id of the piece
+    const int ntok = min(a.bm * kTile, a.rows - tok0);    // valid tokens / ids of the piece
+    const int nvoc = min(nvt * kTile, a.V - voc0);
 
-    // A. dlogits of the block's tiles into its buffer
+    // A. dlogits of the piece's tiles into its buffer
     for (int mi = 0; mi * kTile < ntok; ++mi) {
       for (int nj = 0; nj * kTile < nvoc; ++nj) {
         const int m0 = tok0 + mi * kTile, n0 = voc0 + nj * kTile;
@@ -130,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs
             }
         }
         phase_barrier<false, true>();   // the G tile visible in LDS
-        // full 512-byte rows out to the block buffer: rows mi*256 + r, columns nj*256 ..
+        // full 512-byte rows out to the piece buffer: rows mi*256 + r, columns nj*256 ..
         constexpr int kPerWave = kTile * kTile * 2 / 1024 / kWaves;
         const int ln = opaque_tid() & 63;
 #pragma unroll
@@ -138,14 +132,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs
           const int b = wave * kPerWave + k;
           const int r = 2 * b + (ln >> 5);
           const int c = (ln & 31) ^ (r & 31);
-          *reinterpret_cast<u32x4*>(G + (int64_t)(mi * kTile + r) * kGLd + nj * kTile + 8 * c) =
+          *reinterpret_cast<u32x4*>(G + (int64_t)(mi * kTile + r) * gld + nj * kTile + 8 * c) =
               *reinterpret_cast<const u32x4*>(smem + b * 1024 + 16 * ln);
         }
         phase_barrier<true, true>();    // stores complete, LDS free for the next product
       }
     }
 
-    // B. per 256-wide slice of H: the block's dx tiles and dW tiles, each added once
+    // B. per 256-wide slice of H: the piece's dx tiles and dW tiles, each added once
     for (int hb = 0; hb < a.tiles_h; ++hb) {
       const int h0 = hb * kTile;
       for (int mi = 0; mi * kTile < ntok; ++mi) {   // dx rows tok0 + mi*256 .. = G rows x W
@@ -153,7 +147,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs
         Operand<bf16_t, false> C;   // columns: W[voc0 + v][h0 + h], contraction over v
         Operand<bf16_t, true> R;    // rows: G[mi*256 + token][v]
         C.init(W + (int64_t)voc0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)nvoc * a.H * 2));
-        R.init(G, kGLd, mi * kTile, ntok, (uint32_t)kFusedGBlockBytes);
+        R.init(G, gld, mi * kTile, ntok, gbytes);
         gemm_tile_balanced<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, true>, true>(acc, smem, C, R, 0, nvoc,
                                                                                   opaque_tid());
         atomic_add_tile(acc, make_rsrc(a.dx_acc, (uint32_t)((int64_t)a.rows * a.H * 4)), tok0 + mi * kTile, a.rows, h0,
@@ -164,13 +158,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs
         Operand<bf16_t, false> C;   // columns: x[tok0 + token][h0 + h], contraction over tokens
         Operand<bf16_t, false> R;   // rows: G[token][nj*256 + v]
         C.init(X + (int64_t)tok0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)ntok * a.H * 2));
-        R.init(G, kGLd, nj * kTile, nvoc, (uint32_t)kFusedGBlockBytes);
+        R.init(G, gld, nj * kTile, nvoc, gbytes);
         gemm_tile<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, false>, true>(acc, smem, C, R, 0, ntok,
                                                                          opaque_tid());
         atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V, h0, a.H);
       }
     }
-    __syncthreads();   // every read of this block's buffer is done before the next block writes it
+    __syncthreads();   // every read of this piece's buffer is done before the next piece writes it
   }
 }
 
@@ -203,12 +197,7 @@ static inline int grid_for(int64_t n4) {
 }
 
 hipError_t launch_fused_block(const FusedBlockArgs& a, int grid, hipStream_t s) {
-  const int shape = a.bm * 16 + a.bn;
-  if (shape == 8 * 16 + 4) hipLaunchKernelGGL((fused_block_kernel<8, 4>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (shape == 4 * 16 + 4) hipLaunchKernelGGL((fused_block_kernel<4, 4>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (shape == 4 * 16 + 2) hipLaunchKernelGGL((fused_block_kernel<4, 2>), dim3(grid), dim3(kThreads), 0, s, a);
-  else if (shape == 2 * 16 + 2) hipLaunchKernelGGL((fused_block_kernel<2, 2>), dim3(grid), dim3(kThreads), 0, s, a);
-  else return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fused_block_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -120,16 +120,104 @@ struct FinalizeArgs {
   const Scale* scale;   // loss = sum / scale->denom
 };
 
-// Fused variant, pass 2: a workgroup owns a block of bm x bn tiles of (tokens x vocabulary); it
-// recomputes their logits once, keeps the block's dlogits in its own bf16 buffer in the workspace,
-// then, per 256-wide slice of H, forms whole dx and dW tiles over the block and adds each with one
-// fp32 atomic per element.  The atomic count, rows V H (1 / (256 bn) + 1 / (256 bm)), sets the
-// time (measured at the Llama-3 chunk, fused_bwd per 4096 tokens: 2 x 2 tiles 32.8 ms, 4 x 4 19.2,
-// 4 x 8 18.0, 8 x 4 17.1), so the largest block is best as long as there are enough blocks to keep
-// every compute unit busy.  The shapes the kernel is built for, largest first:
-constexpr int kFusedShapes[4][2] = {{8, 4}, {4, 4}, {4, 2}, {2, 2}};
-constexpr int64_t kFusedGBlockBytes = (int64_t)8 * kTileM * 4 * kTileN * 2;   // 4 MiB: the largest shape's buffer
-constexpr int kFusedMaxGrid = 256;                          // resident workgroups (one per compute unit)
+// Fused variant, pass 2.  The work is a grid of cells: one cell is a row of bm token tiles (bm x 256
+// tokens) by one vocabulary tile.  A workgroup takes its cells in pieces: a piece is bm token tiles by
+// at most bnmax consecutive vocabulary tiles of one row, whose logits it recomputes once, keeps as
+// dlogits in its own bf16 buffer in the workspace, and then turns into whole dx and dW tiles (per
+// 256-wide slice of H) added with one fp32 atomic per element.  A piece of bm x w tiles costs
+// bm x w tile products of each kind and 16 (bm + w) atomic tile adds, so wide, tall pieces are cheap
+// per tile.  Two ways of dealing the pieces:
+//
+// * blocks (BLOCKS): every piece is bm x bn (the last of a row narrower); workgroup L takes blocks
+//   L, L + G, ... in groups of gm rows that sweep the vocabulary (a round of workgroups shares the
+//   group's rows of x and of dx).  Used when the blocks fill the rounds of G workgroups (nearly)
+//   exactly.
+// * spans (SPANS): the workgroups' shares are made equal to within one cell, so that no round is
+//   left partly filled.  The cells are ordered vocabulary super-range first, then row, then
+//   vocabulary tile: super-range s holds tiles [s ws, (s + 1) ws) of every row, ws = ceil(tv / S),
+//   and the segment (s, r) is its part of row r.  With at least as many workgroups as segments,
+//   consecutive workgroups split each segment into near-equal runs; with fewer, each takes whole
+//   consecutive segments.  A run is cut into ceil(n / bnmax) near-equal pieces.  Consecutive
+//   logical workgroups sit on one XCD, so an XCD works on one super-range of every row.
+struct SpanPlan {
+  int blocks;  // 1: blocks of bm x bnmax tiles in groups of gm rows; 0: spans
+  int R;       // rows of cells (token blocks)
+  int tv;      // vocabulary tiles
+  int S;       // vocabulary super-ranges (spans)
+  int gm;      // rows per group (blocks)
+  int G;       // workgroups
+  int bnmax;   // widest piece, in vocabulary tiles (blocks: the block width)
+};
+
+__host__ __device__ inline int span_ws(const SpanPlan& sp) { return (sp.tv + sp.S - 1) / sp.S; }
+__host__ __device__ inline int span_seg_width(const SpanPlan& sp, int i) {
+  const int ws = span_ws(sp), s = i / sp.R;
+  const int hi = (s + 1) * ws < sp.tv ? (s + 1) * ws : sp.tv;
+  return hi - s * ws;
+}
+
+// Super-ranges for tv vocabulary tiles: up to 8 (one per XCD), none of them empty.
+__host__ __device__ inline int span_supers(int tv) {
+  int S = tv < 8 ? tv : 8;
+  while (S > 1 && (S - 1) * ((tv + S - 1) / S) >= tv) --S;
+  return S < 1 ? 1 : S;
+}
+
+// Piece k (0, 1, ...) of logical workgroup L: its row, first vocabulary tile and width in tiles;
+// false once L has no more pieces.  A function of (L, k) alone, so that a kernel carries only k from
+// one piece to the next.
+__host__ __device__ inline bool span_piece(const SpanPlan& sp, int L, int k, int& row, int& vt0, int& nvt) {
+  if (sp.blocks) {
+    const int bn_count = (sp.tv + sp.bnmax - 1) / sp.bnmax;
+    const int blk = L + k * sp.G;
+    if (blk >= sp.R * bn_count) return false;
+    // groups of gm rows (the last group shorter); rows fastest inside a group
+    const int per_group = sp.gm * bn_count;
+    const int g = blk / per_group, first = g * sp.gm;
+    const int rows = sp.R - first < sp.gm ? sp.R - first : sp.gm;
+    const int r = blk - g * per_group;
+    row = first + r % rows;
+    vt0 = (r / rows) * sp.bnmax;
+    nvt = sp.tv - vt0 < sp.bnmax ? sp.tv - vt0 : sp.bnmax;
+    return true;
+  }
+  const int NS = sp.S * sp.R;
+  int i, i_end, k0, k1;
+  if (sp.G >= NS) {   // one run: the workgroup's part of one segment
+    i = (int)((int64_t)L * NS / sp.G);
+    const int first = (int)(((int64_t)i * sp.G + NS - 1) / NS);
+    const int next = (int)(((int64_t)(i + 1) * sp.G + NS - 1) / NS);
+    const int q = next - first, w = span_seg_width(sp, i);
+    i_end = i + 1;
+    k0 = (int)((int64_t)(L - first) * w / q);
+    k1 = (int)((int64_t)(L - first + 1) * w / q);
+  } else {            // whole segments
+    i = (int)((int64_t)L * NS / sp.G);
+    i_end = (int)((int64_t)(L + 1) * NS / sp.G);
+    k0 = 0;
+    k1 = i < i_end ? span_seg_width(sp, i) : 0;
+  }
+  while (i < i_end) {
+    const int n = k1 - k0;
+    const int p = (n + sp.bnmax - 1) / sp.bnmax;
+    if (k < p) {
+      const int a = (int)((int64_t)n * k / p), b = (int)((int64_t)n * (k + 1) / p);
+      row = i % sp.R;
+      vt0 = (i / sp.R) * span_ws(sp) + k0 + a;
+      nvt = b - a;
+      return true;
+    }
+    k -= p;
+    if (++i < i_end) {
+      k0 = 0;
+      k1 = span_seg_width(sp, i);
+    }
+  }
+  return false;
+}
+
+constexpr int kFusedPieceTiles = 48;   // bm x bnmax tiles of bf16 dlogits per workgroup: 6 MiB
+constexpr int kFusedMaxGrid = 256;     // resident workgroups (one per compute unit)
 
 struct FusedBlockArgs {
   const void* x;        // first token row of the launch [rows][H] (bf16)
@@ -138,12 +226,13 @@ struct FusedBlockArgs {
   const float* lse;     // their log-sum-exp [rows]
   float* dx_acc;        // fp32 [rows][H], cleared (or holding the values to add to) before the launch
   float* dw_acc;        // fp32 [V][H], cleared before the first launch of a call
-  char* gbuf;           // [gridDim.x][kFusedGBlockBytes]: each workgroup's dlogits block (bf16)
+  char* gbuf;           // [gridDim.x][gstride]: each workgroup's dlogits piece (bf16, gld per row)
+  int64_t gstride;      // bytes per workgroup: bm 256 rows of gld elements
+  int gld;              // elements per row of a dlogits piece: bnmax 256
   int rows, H, V;
   int tiles_h;
-  int bm, bn;               // block shape in tiles: one of kFusedShapes
-  int blocks_m, blocks_n;   // token blocks of the launch, vocabulary blocks
-  int group_m;              // blocks are walked in groups of group_m token blocks that sweep all vocabulary blocks
+  int bm;               // token tiles per row of cells
+  SpanPlan span;        // span.G == gridDim.x
   Ignore ign;
   const Scale* scale;
 };
