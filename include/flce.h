@@ -71,13 +71,13 @@ typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype_t;
 
 typedef enum {
   FLCE_CHUNKED = 0,           /* token chunks; one [C,V] buffer overwritten in place by dlogits */
-  FLCE_FUSED = 1              /* two passes, no logits buffer: pass 1 per-token log-sum-exp; pass 2
-                                 recomputes the logits tile by tile, turns them into dlogits and
-                                 adds the dx / dW contributions straight into fp32 accumulators
-                                 with atomics.  Each workgroup holds the dlogits of one piece of
-                                 at most 2048 tokens x 1536 vocabulary ids at a time in its own
-                                 buffer of at most 6 MiB (at most 256 of them: 1.5 GiB of
-                                 workspace).  With fp32
+  FLCE_FUSED = 1              /* two passes, logits recomputed: pass 1 per-token log-sum-exp (no
+                                 logits stored); pass 2 cuts the (token x vocabulary) plane into
+                                 blocks of up to 4096 x 4096 and runs in steps: one kernel
+                                 recomputes the logits of up to 1.5 GiB of blocks and stores them
+                                 as dlogits in workspace slots, a second forms the blocks' dx and
+                                 dW tile products and adds them into fp32 accumulators with
+                                 atomics.  With fp32
                                  dx, pass 2 runs once over all N tokens after every chunk's pass 1
                                  (dx is its own accumulator); with bf16 dx, once per chunk into an
                                  fp32 [chunk, H] accumulator.  bf16 inputs

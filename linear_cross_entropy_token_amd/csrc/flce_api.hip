@@ -41,10 +41,9 @@ struct Plan {
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
   size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
   size_t off_gbuf = 0;                   // fused variant: the workgroups' dlogits block buffers
-  int fused_grid = 0;                    // fused variant: resident workgroups of pass 2
-  int fused_bm = 0;                      // fused variant: token tiles per row of pass-2 cells
-  int fused_bnmax = 0;                   // fused variant: widest pass-2 piece, in vocabulary tiles
-  bool fused_blocks = false;             // fused variant: pass-2 pieces dealt as blocks (else spans)
+  int fused_bt = 0, fused_bv = 0;        // fused variant: pass-2 block shape in tiles (tokens, vocabulary)
+  int fused_slots = 0;                   // fused variant: dlogits block slots (blocks per pass-2 step)
+  int64_t fused_slot_bytes = 0;          // fused variant: bytes per slot
   bool fused_all = false;                // fused variant: one pass 2 over all N (fp32 dx) instead of per chunk
   size_t off_scale = 0;                  // flce::Scale of the call
   size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
@@ -208,85 +207,12 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
-// Pass-2 work decomposition over tm token tiles and tv vocabulary tiles with rows of bm token tiles,
-// pieces at most bnmax vocabulary tiles wide (blocks: exactly, the last of a row narrower) and at
-// most gmax workgroups.
-flce::SpanPlan span_plan(int64_t tm, int64_t tv, int bm, int bnmax, int gmax, bool blocks) {
-  flce::SpanPlan sp;
-  sp.blocks = blocks ? 1 : 0;
-  sp.R = (int)cdiv(tm, bm);
-  sp.tv = (int)tv;
-  sp.S = flce::span_supers(sp.tv);
-  sp.gm = std::max(1, 16 / bm);   // block groups of 4096 tokens
-  sp.bnmax = bnmax;
-  const int64_t units = blocks ? (int64_t)sp.R * cdiv(tv, bnmax) : (int64_t)sp.R * tv;
-  sp.G = (int)std::min<int64_t>(gmax, units);
-  return sp;
-}
-
-// Relative cost of a pass-2 piece of h x w tiles: h w tile products of each kind against h + w
-// atomic tile adds per 256-wide slice of H, weighted as the measured block shapes give it (per
-// 4096-token chunk at V = 128,256, H = 4,096: 2 x 2 tiles 32.8 ms, 4 x 4 19.2 ms, 8 x 4 17.1 ms fit
-// about 0.18 ms per tile pair and 0.85 ms per atomic tile add and slice of H).
-constexpr double kAtomicWeight = 4.9;
-
-// The slowest workgroup's cost under a decomposition, and its widest piece.
-double span_cost(const flce::SpanPlan& sp, int64_t tm, int bm, int& maxw) {
-  double worst = 0.0;
-  maxw = 0;
-  for (int L = 0; L < sp.G; ++L) {
-    int r = 0, v0 = 0, n = 0;
-    double cost = 0.0;
-    for (int k = 0; flce::span_piece(sp, L, k, r, v0, n); ++k) {
-      const double h = (double)std::min<int64_t>(bm, tm - (int64_t)r * bm);
-      cost += h * n + kAtomicWeight * (h + n);
-      maxw = std::max(maxw, n);
-    }
-    worst = std::max(worst, cost);
-  }
-  return worst;
-}
-
-// Decomposition of the fused pass 2 over tm token tiles and tv vocabulary tiles.  Blocks of 8 x 6 or
-// 8 x 4 tiles (2048 tokens x 1536 / 1024 vocabulary ids) when they fill the rounds of resident
-// workgroups to 99% (measured: where they do, blocks are up to 8% faster than spans with the same
-// pieces); else spans with the row height (8, 4 or 2 token tiles; widest piece 48 / bm tiles, 6 MiB
-// of bf16 dlogits) whose slowest workgroup costs least.  bnmax ends up as the widest piece used.
-void fused_work(int64_t tm, int64_t tv, bool& blocks, int& bm, int& bnmax) {
-  for (const int bn : {6, 4}) {
-    const int64_t nb = cdiv(tm, 8) * cdiv(tv, bn);
-    const int64_t slots = cdiv(nb, flce::kFusedMaxGrid) * flce::kFusedMaxGrid;
-    if (tm % 8 == 0 && (double)nb >= 0.99 * (double)slots) {
-      blocks = true;
-      bm = 8;
-      bnmax = (int)std::min<int64_t>(bn, tv);
-      return;
-    }
-  }
-  blocks = false;
-  double best = 0.0;
-  bm = 0;
-  for (const int h : {8, 4, 2}) {
-    int w = 0;
-    const double c =
-        span_cost(span_plan(tm, tv, h, flce::kFusedPieceTiles / h, flce::kFusedMaxGrid, false), tm, h, w);
-    if (bm == 0 || c < best) {
-      best = c;
-      bm = h;
-      bnmax = w;
-    }
-  }
-}
-
 // Whether the fused variant runs pass 2 once over all N tokens: dx in fp32 (dx is its own
 // accumulator) and N rows of x and of dx within the kernels' 32-bit buffer offsets.
 bool fused_pass2_over_all(const flce_config_t& cfg, int64_t N, int64_t H) {
   const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
   return cfg.dx_dtype == FLCE_FP32 && N * H * 2 < lim && (N + kTile) * H * 4 < lim;
 }
-
-// Bytes of one workgroup's pass-2 dlogits piece buffer: bm x 256 rows of bnmax x 256 bf16.
-size_t fused_piece_bytes(const Plan& p) { return (size_t)p.fused_bm * kTile * (size_t)p.fused_bnmax * kTile * 2; }
 
 Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_t chunk, bool grads = true,
                bool rms = false) {
@@ -331,13 +257,16 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.off_dwacc = off;
   if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
   p.off_gbuf = off;
-  if (p.fused && grads) {   // one dlogits block buffer per resident workgroup of pass 2
+  if (p.fused && grads) {   // pass 2: dlogits block slots for one step (at most 1.5 GiB)
     p.fused_all = fused_pass2_over_all(cfg, N, H);
-    const int64_t rows = p.fused_all ? N : p.C;
-    fused_work(cdiv(rows, kTile), p.tiles_v, p.fused_blocks, p.fused_bm, p.fused_bnmax);
-    p.fused_grid =
-        span_plan(cdiv(rows, kTile), p.tiles_v, p.fused_bm, p.fused_bnmax, flce::kFusedMaxGrid, p.fused_blocks).G;
-    off = align_up(off + (size_t)p.fused_grid * (size_t)fused_piece_bytes(p));
+    const int64_t tm = cdiv(p.fused_all ? N : p.C, kTile);
+    p.fused_bt = (int)std::min<int64_t>(flce::kFusedBlockTiles, tm);
+    p.fused_bv = (int)std::min<int64_t>(flce::kFusedBlockTiles, p.tiles_v);
+    p.fused_slot_bytes = (int64_t)p.fused_bt * p.fused_bv * kTile * kTile * 2;
+    const int64_t blocks = cdiv(tm, p.fused_bt) * cdiv(p.tiles_v, p.fused_bv);
+    p.fused_slots =
+        (int)std::max<int64_t>(1, std::min<int64_t>(blocks, flce::kFusedSlotBudget / p.fused_slot_bytes));
+    off = align_up(off + (size_t)p.fused_slots * (size_t)p.fused_slot_bytes);
   }
   if (rms) {   // the chunk's normalised rows, their fp32 dL/dx, rstd, dgamma partials and sum
     p.off_xc = off;    off = align_up(off + (size_t)p.C * H * in_size(cfg));
@@ -692,38 +621,46 @@ flce_status_t run_rmsnorm(const Exec& e, const Plan& p, const Opts& o, const voi
   return FLCE_OK;
 }
 
-// Fused variant: per chunk, pass 1 (logits statistics only, no logits store) and pass 2
-// (recompute, dlogits in LDS, dx and dW partials by fp32 atomics); outputs converted last.
-// Pass 2 of the fused variant over `rows` tokens starting at token s: dlogits recomputed block by
-// block and added into dx_acc (rows x H, fp32) and dw_acc (V x H, fp32).
+// Pass 2 of the fused variant over `rows` tokens starting at token s: the (token x vocabulary)
+// plane in blocks of the plan's shape, in steps of up to fused_slots blocks, each step a Z kernel
+// (dlogits of its blocks into the slots) and a P kernel (dx and dW tile products from the slots,
+// added into dx_acc (rows x H, fp32) and dw_acc (V x H, fp32) with atomics).  A launch over fewer
+// tokens than the plan's (the last chunk) has fewer blocks of the same shape.
 flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t s, int64_t rows, const void* x,
                            const void* W, const int64_t* t, const float* lse, float* dx_acc, float* dw_acc,
                            hipStream_t st) {
   const double VH = (double)p.V * (double)p.H;
-  flce::FusedBlockArgs fa{};
+  flce::FusedStepArgs fa{};
   fa.x = static_cast<const char*>(x) + (size_t)s * p.H * 2;
   fa.W = W;
   fa.t = t + s;
   fa.lse = lse + s;
   fa.dx_acc = dx_acc;
   fa.dw_acc = dw_acc;
-  fa.gbuf = e.ws + p.off_gbuf;
+  fa.slots = e.ws + p.off_gbuf;
+  fa.slot_bytes = p.fused_slot_bytes;
   fa.rows = (int)rows;
   fa.H = (int)p.H;
   fa.V = (int)p.V;
-  fa.tiles_h = p.tiles_h;
-  // the plan's row height and widest piece (its buffers are sized for them); a launch over fewer
-  // tokens than the plan's (the last chunk) only has fewer cells
-  fa.bm = p.fused_bm;
-  fa.span = span_plan(cdiv(rows, kTile), p.tiles_v, p.fused_bm, p.fused_bnmax, p.fused_grid, p.fused_blocks);
-  fa.gld = p.fused_bnmax * kTile;
-  fa.gstride = (int64_t)fused_piece_bytes(p);
   fa.ign = o.ign;
   fa.scale = reinterpret_cast<const flce::Scale*>(e.ws + p.off_scale);
-  const int grid = fa.span.G;
-  // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H)
+  flce::StepPlan& sp = fa.sp;
+  sp.tm = (int)cdiv(rows, kTile);
+  sp.tv = p.tiles_v;
+  sp.bt = p.fused_bt;
+  sp.bv = p.fused_bv;
+  sp.blocks_v = (int)cdiv(sp.tv, sp.bv);
+  sp.groups = 8;   // one group per XCD
+  sp.gsize = flce::kFusedGrid / sp.groups;
+  sp.th = p.tiles_h;
+  const int blocks = (int)cdiv(sp.tm, sp.bt) * sp.blocks_v;
+  // recompute (2 rows V H) + dx partials (2 rows V H) + dW partials (2 rows V H), all steps
   FLCE_LAUNCH(mark(e, K_FUSED_BWD, 6.0 * (double)rows * VH, 2.0 * ((double)rows * p.H * 2 + VH * 2), st));
-  FLCE_LAUNCH(flce::launch_fused_block(fa, grid, st));
+  for (int first = 0; first < blocks; first += p.fused_slots) {
+    sp.first = first;
+    sp.count = std::min(p.fused_slots, blocks - first);
+    FLCE_LAUNCH(flce::launch_fused_step(fa, st));
+  }
   return FLCE_OK;
 }
 

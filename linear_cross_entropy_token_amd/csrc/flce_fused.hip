@@ -13,23 +13,23 @@
 namespace flce {
 
 // ---------------------------------------------------------------------------
-// Pass 2.  Each add of a 256 x 256 partial tile into dx or dW costs one fp32 atomic per element;
-// a kernel that added one partial per (token tile, vocabulary tile) pair would make 2 rows V H /
-// 256 adds per chunk (16.8 G at 4096 tokens, V = 128,256, H = 4,096: bound by the atomics).  Here a
-// workgroup works on pieces of bm x w tile pairs (up to 8 x 6: 2048 tokens x 1536 vocabulary ids):
-//   A. it recomputes the piece's logits tiles (contraction over H on the tile engine), turns each
-//      into dlogits G = (exp(z - lse) - onehot) * scale and stores it, bf16, in its own piece
-//      buffer in the workspace (the dlogits tile of the FLCE page's step 2, now for a block of
-//      tiles; it never leaves the workspace and is overwritten by the next piece);
-//   B. for each 256-wide slice of H it forms the piece's bm dx tiles (G rows times W, contraction
-//      over the piece's vocabulary ids) and w dW tiles (G columns times x, contraction over its
-//      tokens) on the same engine and adds each into the fp32 accumulators with atomics (the
-//      reduction by atomic adds of the "Unsloth deep architecture" page's streaming CE kernel).
-// So every dx / dW element receives one atomic per piece that covers it: w x / bm x fewer than
-// with one atomic per tile pair.  The grid is persistent (at most one workgroup per compute unit);
-// span_piece deals the pieces (flce_internal.hpp).  The buffer a
-// workgroup writes is read back only by itself (program order plus a barrier: the writes are
-// complete before any wave reads).
+// Pass 2.  Each add of a 256 x 256 partial tile into dx or dW costs one fp32 atomic per element, and
+// an atomic cannot complete in an XCD's L2 (the eight L2s are not coherent with each other), so it
+// travels to the memory side: a kernel that added one partial per (token tile, vocabulary tile)
+// pair would make 2 rows V H / 256 adds per launch.  Here the plane is cut into blocks of up to
+// 16 x 16 tiles (4096 tokens x 4096 vocabulary ids), 16x fewer adds, done in steps of two kernels
+// (the dealing of blocks and items is StepPlan's, flce_internal.hpp):
+//   Z (fused_z_kernel): each logits tile of the step's blocks is recomputed (contraction over H on
+//     the tile engine) and turned into dlogits G = (exp(z - lse) - onehot) * scale, stored bf16 in
+//     the block's slot (the dlogits tile of the FLCE page's step 2, for a block of tiles; slots are
+//     workspace and are overwritten by the next step);
+//   P (fused_p_kernel): for every 256-wide slice of H, the block's dx tiles (slot rows times W) and
+//     dW tiles (slot columns times x) are formed on the same engine and added into the fp32
+//     accumulators with atomics (the reduction by atomic adds of the "Unsloth deep architecture"
+//     page's streaming CE kernel).
+// The kernel boundary orders the slots' writes before their reads.  A group of workgroups (one
+// XCD's) works on one block at a time, so each slot row or column that a product reads is fetched
+// once into the XCD's L2 for the group's products of it (16 of them, one per slice of H).
 // ---------------------------------------------------------------------------
 
 // Adds a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c] with
@@ -59,112 +59,131 @@ __device__ __forceinline__ void atomic_add_tile(const f32x16 (&acc)[kColBlocks][
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void fused_block_kernel(FusedBlockArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fused_z_kernel(FusedStepArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
+  const StepPlan& sp = a.sp;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  bf16_t* G = reinterpret_cast<bf16_t*>(a.gbuf + (int64_t)L * a.gstride);
+  const int grp = L / sp.gsize, pos = L - grp * sp.gsize;
+  const int gld = sp.bv * kTile;   // bf16 elements per slot row
   const bf16_t* X = static_cast<const bf16_t*>(a.x);
   const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const int gld = a.gld;
-  const uint32_t gbytes = (uint32_t)a.gstride;
-  // Every lane-dependent value below is formed from a fresh opaque_tid() next to its use: this
-  // kernel runs three kinds of tile product in loops, and values hoisted out of those loops would
-  // stay live across every product (each needs nearly all of the register file).
-
-  int row, vt0, nvt;
-  for (int k = 0; span_piece(a.span, L, k, row, vt0, nvt); ++k) {
-    const int tok0 = row * a.bm * kTile;   // first token of the piece (launch-relative)
-    const int voc0 = vt0 * kTile;          // first vocabulary id of the piece
-    const int ntok = min(a.bm * kTile, a.rows - tok0);    // valid tokens / ids of the piece
-    const int nvoc = min(nvt * kTile, a.V - voc0);
-
-    // A. dlogits of the piece's tiles into its buffer
-    for (int mi = 0; mi * kTile < ntok; ++mi) {
-      for (int nj = 0; nj * kTile < nvoc; ++nj) {
-        const int m0 = tok0 + mi * kTile, n0 = voc0 + nj * kTile;
-        f32x16 acc[kColBlocks][4];
-        {
-          Operand<bf16_t, true> C, R;   // columns: W rows (vocabulary), rows: x rows (tokens)
-          C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2));
-          R.init(X, a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * 2));
-          gemm_tile_balanced<bf16_t>(acc, smem, C, R, 0, a.H, opaque_tid());
-        }
-        // G tile into LDS as 256 rows of 512 bytes, 16-byte chunk c of row r at c ^ (r % 32)
-        const int tid = opaque_tid();
-        const Frag f = frag_coords(tid);
-        const int lane = tid & 63;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = f.row(j);
-          const int tok = m0 + row;
-          const int64_t tv = tok < a.rows ? a.t[tok] : -1;
-          const bool rok = tok < a.rows && !a.ign.skip(tv);   // an ignored token's row of G is zero
-          const float l = rok ? a.lse[tok] : 0.f;
-          const float gscale = a.scale->grad;
-#pragma unroll
-          for (int i = 0; i < kColBlocks; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int c0 = f.col0(i, q);
-              float gv[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int v = n0 + c0 + e;
-                float g = 0.f;
-                if (rok && v < a.V) {
-                  g = fast_exp(acc[i][j][4 * q + e] - l);
-                  if (v == tv) g -= 1.f;
-                  g *= gscale;
-                }
-                gv[e] = g;
-              }
-              *reinterpret_cast<u32x2*>(smem + row * 512 + (((c0 >> 3) ^ (row & 31)) << 4) + 8 * (lane >> 5)) =
-                  u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-            }
-        }
-        phase_barrier<false, true>();   // the G tile visible in LDS
-        // full 512-byte rows out to the piece buffer: rows mi*256 + r, columns nj*256 ..
-        constexpr int kPerWave = kTile * kTile * 2 / 1024 / kWaves;
-        const int ln = opaque_tid() & 63;
-#pragma unroll
-        for (int k = 0; k < kPerWave; ++k) {
-          const int b = wave * kPerWave + k;
-          const int r = 2 * b + (ln >> 5);
-          const int c = (ln & 31) ^ (r & 31);
-          *reinterpret_cast<u32x4*>(G + (int64_t)(mi * kTile + r) * gld + nj * kTile + 8 * c) =
-              *reinterpret_cast<const u32x4*>(smem + b * 1024 + 16 * ln);
-        }
-        phase_barrier<true, true>();    // stores complete, LDS free for the next product
+  int seen = 0;   // items of the group's earlier blocks
+  for (int j = grp; j < sp.count; j += sp.groups) {
+    int mt0, vt0, nt, nv;
+    step_block(sp, j, mt0, vt0, nt, nv);
+    const int n = z_items(nt, nv);
+    bf16_t* G = reinterpret_cast<bf16_t*>(a.slots + (int64_t)j * a.slot_bytes);
+    int q = (pos - seen) % sp.gsize;
+    if (q < 0) q += sp.gsize;
+    for (; q < n; q += sp.gsize) {
+      int mi, nj;
+      grid_item(q, nt, nv, 4, mi, nj);
+      const int m0 = (mt0 + mi) * kTile, n0 = (vt0 + nj) * kTile;   // first token, first vocabulary id
+      f32x16 acc[kColBlocks][4];
+      {
+        Operand<bf16_t, true> C, R;   // columns: W rows (vocabulary), rows: x rows (tokens)
+        C.init(W, a.H, n0, a.V, (uint32_t)((int64_t)a.V * a.H * 2));
+        R.init(X, a.H, m0, a.rows, (uint32_t)((int64_t)a.rows * a.H * 2));
+        gemm_tile_balanced<bf16_t>(acc, smem, C, R, 0, a.H, opaque_tid());
       }
+      // G tile into LDS as 256 rows of 512 bytes, 16-byte chunk c of row r at c ^ (r % 32)
+      const int tid = opaque_tid();
+      const Frag f = frag_coords(tid);
+      const int lane = tid & 63;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int row = f.row(jj);
+        const int tok = m0 + row;
+        const int64_t tv = tok < a.rows ? a.t[tok] : -1;
+        const bool rok = tok < a.rows && !a.ign.skip(tv);   // an ignored token's row of G is zero
+        const float l = rok ? a.lse[tok] : 0.f;
+        const float gscale = a.scale->grad;
+#pragma unroll
+        for (int i = 0; i < kColBlocks; ++i)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int c0 = f.col0(i, qq);
+            float gv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int v = n0 + c0 + e;
+              float g = 0.f;
+              if (rok && v < a.V) {
+                g = fast_exp(acc[i][jj][4 * qq + e] - l);
+                if (v == tv) g -= 1.f;
+                g *= gscale;
+              }
+              gv[e] = g;
+            }
+            *reinterpret_cast<u32x2*>(smem + row * 512 + (((c0 >> 3) ^ (row & 31)) << 4) + 8 * (lane >> 5)) =
+                u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+          }
+      }
+      phase_barrier<false, true>();   // the G tile visible in LDS
+      // full 512-byte rows out to the slot: rows mi*256 + r, columns nj*256 ..
+      constexpr int kPerWave = kTile * kTile * 2 / 1024 / kWaves;
+      const int ln = opaque_tid() & 63;
+#pragma unroll
+      for (int k = 0; k < kPerWave; ++k) {
+        const int b = wave * kPerWave + k;
+        const int r = 2 * b + (ln >> 5);
+        const int c = (ln & 31) ^ (r & 31);
+        *reinterpret_cast<u32x4*>(G + (int64_t)(mi * kTile + r) * gld + nj * kTile + 8 * c) =
+            *reinterpret_cast<const u32x4*>(smem + b * 1024 + 16 * ln);
+      }
+      phase_barrier<true, true>();    // stores complete, LDS free for the next product
     }
+    seen += n;
+  }
+}
 
-    // B. per 256-wide slice of H: the piece's dx tiles and dW tiles, each added once
-    for (int hb = 0; hb < a.tiles_h; ++hb) {
-      const int h0 = hb * kTile;
-      for (int mi = 0; mi * kTile < ntok; ++mi) {   // dx rows tok0 + mi*256 .. = G rows x W
-        f32x16 acc[kColBlocks][4];
-        Operand<bf16_t, false> C;   // columns: W[voc0 + v][h0 + h], contraction over v
+__global__ __launch_bounds__(kThreads, 1) void fused_p_kernel(FusedStepArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
+  const StepPlan& sp = a.sp;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = L / sp.gsize, pos = L - grp * sp.gsize;
+  const int gld = sp.bv * kTile;
+  const uint32_t gbytes = (uint32_t)a.slot_bytes;
+  const bf16_t* X = static_cast<const bf16_t*>(a.x);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
+  int seen = 0;
+  for (int j = grp; j < sp.count; j += sp.groups) {
+    int mt0, vt0, nt, nv;
+    step_block(sp, j, mt0, vt0, nt, nv);
+    const int n = p_items(sp, nt, nv);
+    const bf16_t* G = reinterpret_cast<const bf16_t*>(a.slots + (int64_t)j * a.slot_bytes);
+    const int tok0 = mt0 * kTile, voc0 = vt0 * kTile;
+    const int ntok = min(nt * kTile, a.rows - tok0), nvoc = min(nv * kTile, a.V - voc0);
+    int q = (pos - seen) % sp.gsize;
+    if (q < 0) q += sp.gsize;
+    for (; q < n; q += sp.gsize) {
+      f32x16 acc[kColBlocks][4];
+      if (q < nt * sp.th) {   // dx rows tok0 + mi*256 .. = G rows x W, contraction over the block's ids
+        int mi, hb;
+        grid_item(q, nt, sp.th, 4, mi, hb);
+        Operand<bf16_t, false> C;   // columns: W[voc0 + v][h0 + h]
         Operand<bf16_t, true> R;    // rows: G[mi*256 + token][v]
-        C.init(W + (int64_t)voc0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)nvoc * a.H * 2));
+        C.init(W + (int64_t)voc0 * a.H, a.H, hb * kTile, a.H, (uint32_t)((int64_t)nvoc * a.H * 2));
         R.init(G, gld, mi * kTile, ntok, gbytes);
         gemm_tile_balanced<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, true>, true>(acc, smem, C, R, 0, nvoc,
                                                                                   opaque_tid());
-        atomic_add_tile(acc, make_rsrc(a.dx_acc, (uint32_t)((int64_t)a.rows * a.H * 4)), tok0 + mi * kTile, a.rows, h0,
-                        a.H);
-      }
-      for (int nj = 0; nj * kTile < nvoc; ++nj) {   // dW rows voc0 + nj*256 .. = G columns^T x
-        f32x16 acc[kColBlocks][4];
-        Operand<bf16_t, false> C;   // columns: x[tok0 + token][h0 + h], contraction over tokens
+        atomic_add_tile(acc, make_rsrc(a.dx_acc, (uint32_t)((int64_t)a.rows * a.H * 4)), tok0 + mi * kTile, a.rows,
+                        hb * kTile, a.H);
+      } else {                // dW rows voc0 + nj*256 .. = G columns^T x, contraction over the block's tokens
+        int nj, hb;
+        grid_item(q - nt * sp.th, nv, sp.th, 4, nj, hb);
+        Operand<bf16_t, false> C;   // columns: x[tok0 + token][h0 + h]
         Operand<bf16_t, false> R;   // rows: G[token][nj*256 + v]
-        C.init(X + (int64_t)tok0 * a.H, a.H, h0, a.H, (uint32_t)((int64_t)ntok * a.H * 2));
+        C.init(X + (int64_t)tok0 * a.H, a.H, hb * kTile, a.H, (uint32_t)((int64_t)ntok * a.H * 2));
         R.init(G, gld, nj * kTile, nvoc, gbytes);
         gemm_tile<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, false>, true>(acc, smem, C, R, 0, ntok,
                                                                          opaque_tid());
-        atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V, h0, a.H);
+        atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V,
+                        hb * kTile, a.H);
       }
     }
-    __syncthreads();   // every read of this piece's buffer is done before the next piece writes it
+    seen += n;
   }
 }
 
@@ -196,8 +215,12 @@ static inline int grid_for(int64_t n4) {
   return (int)(b < 1 ? 1 : b);
 }
 
-hipError_t launch_fused_block(const FusedBlockArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(fused_block_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+hipError_t launch_fused_step(const FusedStepArgs& a, hipStream_t s) {
+  const int grid = a.sp.groups * a.sp.gsize;
+  hipLaunchKernelGGL(fused_z_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fused_p_kernel, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -120,119 +120,83 @@ struct FinalizeArgs {
   const Scale* scale;   // loss = sum / scale->denom
 };
 
-// Fused variant, pass 2.  The work is a grid of cells: one cell is a row of bm token tiles (bm x 256
-// tokens) by one vocabulary tile.  A workgroup takes its cells in pieces: a piece is bm token tiles by
-// at most bnmax consecutive vocabulary tiles of one row, whose logits it recomputes once, keeps as
-// dlogits in its own bf16 buffer in the workspace, and then turns into whole dx and dW tiles (per
-// 256-wide slice of H) added with one fp32 atomic per element.  A piece of bm x w tiles costs
-// bm x w tile products of each kind and 16 (bm + w) atomic tile adds, so wide, tall pieces are cheap
-// per tile.  Two ways of dealing the pieces:
-//
-// * blocks (BLOCKS): every piece is bm x bn (the last of a row narrower); workgroup L takes blocks
-//   L, L + G, ... in groups of gm rows that sweep the vocabulary (a round of workgroups shares the
-//   group's rows of x and of dx).  Used when the blocks fill the rounds of G workgroups (nearly)
-//   exactly.
-// * spans (SPANS): the workgroups' shares are made equal to within one cell, so that no round is
-//   left partly filled.  The cells are ordered vocabulary super-range first, then row, then
-//   vocabulary tile: super-range s holds tiles [s ws, (s + 1) ws) of every row, ws = ceil(tv / S),
-//   and the segment (s, r) is its part of row r.  With at least as many workgroups as segments,
-//   consecutive workgroups split each segment into near-equal runs; with fewer, each takes whole
-//   consecutive segments.  A run is cut into ceil(n / bnmax) near-equal pieces.  Consecutive
-//   logical workgroups sit on one XCD, so an XCD works on one super-range of every row.
-struct SpanPlan {
-  int blocks;  // 1: blocks of bm x bnmax tiles in groups of gm rows; 0: spans
-  int R;       // rows of cells (token blocks)
-  int tv;      // vocabulary tiles
-  int S;       // vocabulary super-ranges (spans)
-  int gm;      // rows per group (blocks)
-  int G;       // workgroups
-  int bnmax;   // widest piece, in vocabulary tiles (blocks: the block width)
+// Fused variant, pass 2.  The (token x vocabulary) plane of a launch is cut into blocks of bt x bv
+// tiles (up to 16 x 16: 4096 tokens x 4096 vocabulary ids), taken row by row (token blocks outer) in
+// steps of up to `slots` blocks.  Per step, two kernels:
+//   Z: recompute every logits tile of the step's blocks and store it as bf16 dlogits in the block's
+//      slot buffer (bt 256 rows x bv 256 columns);
+//   P: form the blocks' dx tiles (slot rows times W, contraction over the block's vocabulary ids)
+//      and dW tiles (slot columns times x, contraction over its tokens) for every 256-wide slice of
+//      H and add each into the fp32 accumulators with one atomic per element.
+// Every dx / dW element thus receives one atomic per vocabulary / token block.  In both kernels the
+// workgroups form `groups` groups of `gsize` (one group per XCD: consecutive logical workgroups sit
+// on one XCD); group g takes the step's blocks g, g + groups, ... and its workgroups deal each
+// block's items round-robin, so that a group works on one block at a time and its L2 shares that
+// block's dlogits and operand strips.
+struct StepPlan {
+  int tm, tv;         // token and vocabulary tiles of the launch
+  int bt, bv;         // block shape in tiles
+  int blocks_v;       // vocabulary blocks per token block: ceil(tv / bv)
+  int first, count;   // the step's blocks: first (global index) .. first + count - 1
+  int groups, gsize;  // workgroup groups and their size (groups * gsize = gridDim.x)
+  int th;             // 256-wide slices of H
 };
 
-__host__ __device__ inline int span_ws(const SpanPlan& sp) { return (sp.tv + sp.S - 1) / sp.S; }
-__host__ __device__ inline int span_seg_width(const SpanPlan& sp, int i) {
-  const int ws = span_ws(sp), s = i / sp.R;
-  const int hi = (s + 1) * ws < sp.tv ? (s + 1) * ws : sp.tv;
-  return hi - s * ws;
+// Row-major grid of TM x TN items dealt in groups of gm rows, rows fastest inside a group (the
+// tile order that lets consecutive items share operand strips).
+__host__ __device__ inline void grid_item(int q, int TM, int TN, int gm, int& m, int& n) {
+  const int per_group = gm * TN;
+  const int g = q / per_group, first = g * gm;
+  const int rows = TM - first < gm ? TM - first : gm;
+  const int r = q - g * per_group;
+  m = first + r % rows;
+  n = r / rows;
 }
 
-// Super-ranges for tv vocabulary tiles: up to 8 (one per XCD), none of them empty.
-__host__ __device__ inline int span_supers(int tv) {
-  int S = tv < 8 ? tv : 8;
-  while (S > 1 && (S - 1) * ((tv + S - 1) / S) >= tv) --S;
-  return S < 1 ? 1 : S;
+// Block j (0 .. count - 1) of the step: its first token tile, first vocabulary tile, and extents.
+__host__ __device__ inline void step_block(const StepPlan& sp, int j, int& mt0, int& vt0, int& nt, int& nv) {
+  const int b = sp.first + j;
+  const int r = b / sp.blocks_v, c = b - r * sp.blocks_v;
+  mt0 = r * sp.bt;
+  vt0 = c * sp.bv;
+  nt = sp.tm - mt0 < sp.bt ? sp.tm - mt0 : sp.bt;
+  nv = sp.tv - vt0 < sp.bv ? sp.tv - vt0 : sp.bv;
 }
 
-// Piece k (0, 1, ...) of logical workgroup L: its row, first vocabulary tile and width in tiles;
-// false once L has no more pieces.  A function of (L, k) alone, so that a kernel carries only k from
-// one piece to the next.
-__host__ __device__ inline bool span_piece(const SpanPlan& sp, int L, int k, int& row, int& vt0, int& nvt) {
-  if (sp.blocks) {
-    const int bn_count = (sp.tv + sp.bnmax - 1) / sp.bnmax;
-    const int blk = L + k * sp.G;
-    if (blk >= sp.R * bn_count) return false;
-    // groups of gm rows (the last group shorter); rows fastest inside a group
-    const int per_group = sp.gm * bn_count;
-    const int g = blk / per_group, first = g * sp.gm;
-    const int rows = sp.R - first < sp.gm ? sp.R - first : sp.gm;
-    const int r = blk - g * per_group;
-    row = first + r % rows;
-    vt0 = (r / rows) * sp.bnmax;
-    nvt = sp.tv - vt0 < sp.bnmax ? sp.tv - vt0 : sp.bnmax;
-    return true;
+// Items of a block in each kernel: Z, its logits tiles; P, its dx and dW tile products.
+__host__ __device__ inline int z_items(int nt, int nv) { return nt * nv; }
+__host__ __device__ inline int p_items(const StepPlan& sp, int nt, int nv) { return (nt + nv) * sp.th; }
+
+// Walks the items of workgroup (group g, position w): calls f(j, q) for block j's item q.
+template <bool PRODUCTS, class F>
+__host__ __device__ inline void step_items(const StepPlan& sp, int g, int w, F&& f) {
+  int seen = 0;   // items of the group's earlier blocks
+  for (int j = g; j < sp.count; j += sp.groups) {
+    int mt0, vt0, nt, nv;
+    step_block(sp, j, mt0, vt0, nt, nv);
+    const int n = PRODUCTS ? p_items(sp, nt, nv) : z_items(nt, nv);
+    int q = (w - seen) % sp.gsize;
+    if (q < 0) q += sp.gsize;
+    for (; q < n; q += sp.gsize) f(j, q);
+    seen += n;
   }
-  const int NS = sp.S * sp.R;
-  int i, i_end, k0, k1;
-  if (sp.G >= NS) {   // one run: the workgroup's part of one segment
-    i = (int)((int64_t)L * NS / sp.G);
-    const int first = (int)(((int64_t)i * sp.G + NS - 1) / NS);
-    const int next = (int)(((int64_t)(i + 1) * sp.G + NS - 1) / NS);
-    const int q = next - first, w = span_seg_width(sp, i);
-    i_end = i + 1;
-    k0 = (int)((int64_t)(L - first) * w / q);
-    k1 = (int)((int64_t)(L - first + 1) * w / q);
-  } else {            // whole segments
-    i = (int)((int64_t)L * NS / sp.G);
-    i_end = (int)((int64_t)(L + 1) * NS / sp.G);
-    k0 = 0;
-    k1 = i < i_end ? span_seg_width(sp, i) : 0;
-  }
-  while (i < i_end) {
-    const int n = k1 - k0;
-    const int p = (n + sp.bnmax - 1) / sp.bnmax;
-    if (k < p) {
-      const int a = (int)((int64_t)n * k / p), b = (int)((int64_t)n * (k + 1) / p);
-      row = i % sp.R;
-      vt0 = (i / sp.R) * span_ws(sp) + k0 + a;
-      nvt = b - a;
-      return true;
-    }
-    k -= p;
-    if (++i < i_end) {
-      k0 = 0;
-      k1 = span_seg_width(sp, i);
-    }
-  }
-  return false;
 }
 
-constexpr int kFusedPieceTiles = 48;   // bm x bnmax tiles of bf16 dlogits per workgroup: 6 MiB
-constexpr int kFusedMaxGrid = 256;     // resident workgroups (one per compute unit)
+constexpr int kFusedBlockTiles = 16;   // block side in tiles (4096 tokens / vocabulary ids)
+constexpr int64_t kFusedSlotBudget = (int64_t)3 << 29;   // 1.5 GiB of dlogits slots per step
+constexpr int kFusedGrid = 256;        // workgroups of each pass-2 kernel
 
-struct FusedBlockArgs {
+struct FusedStepArgs {
   const void* x;        // first token row of the launch [rows][H] (bf16)
   const void* W;        // [V][H] (bf16)
   const int64_t* t;     // targets of those rows [rows]
   const float* lse;     // their log-sum-exp [rows]
-  float* dx_acc;        // fp32 [rows][H], cleared (or holding the values to add to) before the launch
+  float* dx_acc;        // fp32 [rows][H], cleared (or holding the values to add to) before the first step
   float* dw_acc;        // fp32 [V][H], cleared before the first launch of a call
-  char* gbuf;           // [gridDim.x][gstride]: each workgroup's dlogits piece (bf16, gld per row)
-  int64_t gstride;      // bytes per workgroup: bm 256 rows of gld elements
-  int gld;              // elements per row of a dlogits piece: bnmax 256
+  char* slots;          // [count][slot_bytes]: the step's dlogits blocks (bf16, bv 256 per row)
+  int64_t slot_bytes;
   int rows, H, V;
-  int tiles_h;
-  int bm;               // token tiles per row of cells
-  SpanPlan span;        // span.G == gridDim.x
+  StepPlan sp;
   Ignore ign;
   const Scale* scale;
 };
@@ -287,7 +251,7 @@ hipError_t launch_dx(In in, const DxArgs& a, hipStream_t s);
 hipError_t launch_dx_reduce(const DxReduceArgs& a, hipStream_t s);
 hipError_t launch_dw(In in, const DwArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
-hipError_t launch_fused_block(const FusedBlockArgs& a, int grid, hipStream_t s);
+hipError_t launch_fused_step(const FusedStepArgs& a, hipStream_t s);   // the step's Z then P kernel
 hipError_t launch_fill_zero(const FillArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const CastArgs& a, hipStream_t s);
 hipError_t launch_scale(const ScaleArgs& a, hipStream_t s);

@@ -1,73 +1,97 @@
-// Host-side check of the fused variant's pass-2 work decomposition (span_piece in
-// flce_internal.hpp): for many problem shapes, row heights, piece widths and workgroup counts, in
-// both dealing modes, every cell (row of token tiles x vocabulary tile) is covered by exactly one
-// piece of exactly one workgroup, and every piece lies inside the grid and is at most bnmax wide.
-// Spans must also give every workgroup the same number of cells to within one per segment it
-// touches.  Prints "PASS pass2 <cases>" and exits 0, or prints the first failure and exits 1.
+// Host-side check of the fused variant's pass-2 work dealing (StepPlan, step_block, step_items and
+// grid_item in flce_internal.hpp): for many launch shapes, block shapes, step sizes and workgroup
+// groupings, every block of the plane is in exactly one step, every logits tile (Z kernel) and every
+// dx / dW tile product (P kernel) of a step's blocks is dealt to exactly one workgroup, each item
+// decodes to a tile inside its block, and a group's workgroups get the same number of items to
+// within one per block.  Prints "PASS pass2 <cases>" and exits 0, or the first failure and exits 1.
 #include "flce_internal.hpp"
 
 #include <algorithm>
 #include <cstdio>
 #include <vector>
 
+static int fail(const char* what, int tm, int tv, int bt, int bv, int slots, int groups, int gsize) {
+  std::printf("FAIL %s: tm=%d tv=%d bt=%d bv=%d slots=%d groups=%d gsize=%d\n", what, tm, tv, bt, bv, slots, groups,
+              gsize);
+  return 1;
+}
+
 int main() {
   long cases = 0;
-  // token tiles: small, around multiples of the row heights, and the long-context 512; vocabulary
-  // tiles: small and the Llama-2 / Llama-3 / Qwen3 vocabularies (125, 501, 594) and their neighbours
-  const int tms[] = {1, 2, 3, 4, 5, 6, 7, 8, 9, 15, 16, 17, 31, 32, 33, 64, 65, 127, 512};
-  const int tvs[] = {1, 2, 3, 5, 7, 8, 9, 10, 15, 16, 17, 20, 31, 33, 63, 64, 125, 126, 255, 500, 501, 594, 627};
+  const int tms[] = {1, 2, 3, 7, 8, 15, 16, 17, 31, 33, 64, 65, 512};
+  const int tvs[] = {1, 2, 5, 12, 16, 17, 63, 125, 126, 501, 594};
+  const int ths[] = {3, 16};
   for (int tm : tms)
     for (int tv : tvs)
-      for (int bm : {8, 4, 2})
-        for (int bnmax : {1, 2, 3, 5, 6, 12, 24})
-          for (int gmax : {1, 7, 255, 256})
-            for (int blocks : {0, 1}) {
-              if (tm == 512 && bnmax < 5) continue;   // the long-context rows with realistic pieces only
-              flce::SpanPlan sp;
-              sp.blocks = blocks;
-              sp.R = (tm + bm - 1) / bm;
-              sp.tv = tv;
-              sp.S = flce::span_supers(tv);
-              sp.gm = std::max(1, 16 / bm);
-              sp.bnmax = bnmax;
-              const int64_t units = blocks ? (int64_t)sp.R * ((tv + bnmax - 1) / bnmax) : (int64_t)sp.R * tv;
-              sp.G = (int)std::min<int64_t>(gmax, units);
-              if (sp.S < 1 || sp.S > 8 || (sp.S > 1 && (sp.S - 1) * ((tv + sp.S - 1) / sp.S) >= tv)) {
-                std::printf("FAIL empty super-range tv=%d S=%d\n", tv, sp.S);
-                return 1;
-              }
-              std::vector<int> cover((size_t)sp.R * tv, 0);
-              int lo = 1 << 30, hi = 0;
-              for (int L = 0; L < sp.G; ++L) {
-                int r = 0, v0 = 0, n = 0, cells = 0;
-                for (int k = 0; flce::span_piece(sp, L, k, r, v0, n); ++k) {
-                  if (n < 1 || n > bnmax || r < 0 || r >= sp.R || v0 < 0 || v0 + n > tv) {
-                    std::printf("FAIL piece tm=%d tv=%d bm=%d bnmax=%d G=%d blocks=%d L=%d: row %d tiles %d+%d\n", tm,
-                                tv, bm, bnmax, sp.G, blocks, L, r, v0, n);
-                    return 1;
+      for (int bt : {1, 4, 16})
+        for (int bv : {1, 5, 16})
+          for (int slots : {3, 48, 1000})
+            for (int groups : {1, 8})
+              for (int gsize : {7, 32})
+                for (int th : ths) {
+                  if (tm == 512 && (bt < 16 || bv < 16)) continue;   // long-context rows: the real shape only
+                  flce::StepPlan sp;
+                  sp.tm = tm;
+                  sp.tv = tv;
+                  sp.bt = std::min(bt, tm);
+                  sp.bv = std::min(bv, tv);
+                  sp.blocks_v = (tv + sp.bv - 1) / sp.bv;
+                  sp.groups = groups;
+                  sp.gsize = gsize;
+                  sp.th = th;
+                  const int blocks = ((tm + sp.bt - 1) / sp.bt) * sp.blocks_v;
+                  std::vector<int> zcov((size_t)tm * tv, 0);
+                  std::vector<int> pcov_dx((size_t)tm * th, 0), pcov_dw((size_t)tv * th, 0);
+                  for (int first = 0; first < blocks; first += slots) {
+                    sp.first = first;
+                    sp.count = std::min(slots, blocks - first);
+                    for (int kind = 0; kind < 2; ++kind) {
+                      std::vector<int> per((size_t)groups * gsize, 0);
+                      for (int g = 0; g < groups; ++g)
+                        for (int w = 0; w < gsize; ++w) {
+                          auto visit = [&](int j, int q) {
+                            int mt0, vt0, nt, nv;
+                            flce::step_block(sp, j, mt0, vt0, nt, nv);
+                            per[(size_t)g * gsize + w]++;
+                            if (kind == 0) {
+                              int mi, nj;
+                              flce::grid_item(q, nt, nv, 4, mi, nj);
+                              if (mi < 0 || mi >= nt || nj < 0 || nj >= nv) return;
+                              zcov[(size_t)(mt0 + mi) * tv + vt0 + nj]++;
+                            } else if (q < nt * th) {
+                              int mi, hb;
+                              flce::grid_item(q, nt, th, 4, mi, hb);
+                              if (mi < 0 || mi >= nt || hb < 0 || hb >= th) return;
+                              pcov_dx[(size_t)(mt0 + mi) * th + hb]++;
+                            } else {
+                              int nj, hb;
+                              flce::grid_item(q - nt * th, nv, th, 4, nj, hb);
+                              if (nj < 0 || nj >= nv || hb < 0 || hb >= th) return;
+                              // a vocabulary tile's dW products: one per token block containing it
+                              pcov_dw[(size_t)(vt0 + nj) * th + hb]++;
+                            }
+                          };
+                          if (kind == 0) flce::step_items<false>(sp, g, w, visit);
+                          else flce::step_items<true>(sp, g, w, visit);
+                        }
+                      // balance inside each group: within one item per block the group holds
+                      for (int g = 0; g < groups; ++g) {
+                        const int nb = (sp.count - g + groups - 1) / groups;
+                        const auto b = per.begin() + (size_t)g * gsize;
+                        const int lo = *std::min_element(b, b + gsize), hi = *std::max_element(b, b + gsize);
+                        if (nb > 0 && hi - lo > nb) return fail("unbalanced group", tm, tv, bt, bv, slots, groups, gsize);
+                      }
+                    }
                   }
-                  for (int k = 0; k < n; ++k) cover[(size_t)r * tv + v0 + k]++;
-                  cells += n;
+                  const int token_blocks = (tm + sp.bt - 1) / sp.bt;
+                  for (int c : zcov)
+                    if (c != 1) return fail("logits tile not dealt exactly once", tm, tv, bt, bv, slots, groups, gsize);
+                  for (int c : pcov_dx)
+                    if (c != sp.blocks_v) return fail("dx product count", tm, tv, bt, bv, slots, groups, gsize);
+                  for (int c : pcov_dw)
+                    if (c != token_blocks) return fail("dW product count", tm, tv, bt, bv, slots, groups, gsize);
+                  ++cases;
                 }
-                lo = std::min(lo, cells);
-                hi = std::max(hi, cells);
-              }
-              for (size_t i = 0; i < cover.size(); ++i)
-                if (cover[i] != 1) {
-                  std::printf("FAIL cell %zu covered %d times: tm=%d tv=%d bm=%d bnmax=%d G=%d blocks=%d\n", i,
-                              cover[i], tm, tv, bm, bnmax, sp.G, blocks);
-                  return 1;
-                }
-              // spans with at least one segment per workgroup: one run per workgroup, equal to within
-              // the rounding of one segment's split (the segment widths differ by at most one tile
-              // except the last super-range, which may be narrower)
-              const int NS = sp.S * sp.R;
-              if (!blocks && sp.G >= NS && hi - lo > (tv + sp.S - 1) / sp.S) {
-                std::printf("FAIL unbalanced spans tm=%d tv=%d bm=%d G=%d: %d..%d cells\n", tm, tv, bm, sp.G, lo, hi);
-                return 1;
-              }
-              ++cases;
-            }
   std::printf("PASS pass2 %ld\n", cases);
   return 0;
 }

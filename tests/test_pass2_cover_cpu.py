@@ -1,8 +1,8 @@
-"""The fused variant's pass-2 work decomposition, checked on the host (CPU only): tests/c/pass2_cover.cpp
-includes the library's own span_piece and checks, over a grid of shapes, row heights, piece widths and
-workgroup counts in both dealing modes, that every cell is covered exactly once by pieces inside the
-grid and no wider than allowed (an overlap would make two workgroups add the same dlogits twice; a
-gap would drop a tile's dx and dW contributions)."""
+"""The fused variant's pass-2 work dealing, checked on the host (CPU only): tests/c/pass2_cover.cpp
+includes the library's own StepPlan functions and checks, over a grid of launch shapes, block shapes,
+step sizes and workgroup groupings, that every logits tile is recomputed exactly once and every dx
+tile gets one product per vocabulary block and every dW tile one per token block (a duplicate would
+add a contribution twice; a gap would drop one), each dealt to exactly one workgroup."""
 import os
 import subprocess
 
