@@ -207,6 +207,63 @@ int64_t effective_chunk(int64_t N, int64_t H, int64_t V, int64_t chunk, int64_t 
   return std::min(c, N);
 }
 
+// Pass 2 of the fused variant over tm token tiles and tv vocabulary tiles with blocks of bt x bv
+// tiles: the slots of a step (as many blocks as 1.5 GiB holds, a multiple of the 8 workgroup groups
+// when there are that many, so that every group (XCD) gets the same number of a step's blocks).
+int64_t fused_slots_for(int64_t tm, int64_t tv, int bt, int bv) {
+  const int64_t blocks = cdiv(tm, bt) * cdiv(tv, bv);
+  int64_t slots = std::min<int64_t>(blocks, flce::kFusedSlotBudget / ((int64_t)bt * bv * kTile * kTile * 2));
+  if (slots > 8) slots -= slots % 8;
+  return std::max<int64_t>(1, slots);
+}
+
+// Relative time of pass 2 with blocks of bt x bv tiles: over the steps, the busiest group's blocks,
+// each costing its tile pairs (one logits tile and its share of the dx and dW products) plus
+// kAtomicWeight per tile of its two atomic streams.  The weight is fitted to the block shapes
+// measured on the Llama-3, Qwen3, long-context and Llama-2 workloads (16 x 16, 32 x 16, 16 x 32,
+// 32 x 32 and 24 x 24 tiles), whose pass-2 times it orders correctly.
+constexpr double kAtomicWeight = 0.93;
+double fused_cost(int64_t tm, int64_t tv, int bt, int bv) {
+  const int64_t bvn = cdiv(tv, bv), nb = cdiv(tm, bt) * bvn, slots = fused_slots_for(tm, tv, bt, bv);
+  double total = 0.0;
+  for (int64_t first = 0; first < nb; first += slots) {
+    const int64_t count = std::min(slots, nb - first);
+    double worst = 0.0;
+    for (int64_t g = 0; g < 8; ++g) {
+      double w = 0.0;
+      for (int64_t j = g; j < count; j += 8) {
+        const int64_t b = first + j, r = b / bvn, c = b - r * bvn;
+        const double nt = (double)std::min<int64_t>(bt, tm - r * bt), nv = (double)std::min<int64_t>(bv, tv - c * bv);
+        w += nt * nv + kAtomicWeight * (nt + nv);
+      }
+      worst = std::max(worst, w);
+    }
+    total += worst;
+  }
+  return total;
+}
+
+// Block shape of pass 2: heights of 32, 16 or 8 token tiles, widths of 8 .. 48 vocabulary tiles, at
+// most 1536 tiles (192 MiB of slot, so that a step holds at least 8 blocks); the cheapest under
+// fused_cost, the larger block (fewer atomics) on a tie.
+void fused_block_shape(int64_t tm, int64_t tv, int& bt, int& bv) {
+  double best = 0.0;
+  bt = bv = 0;
+  for (const int h0 : {32, 16, 8}) {
+    const int h = (int)std::min<int64_t>(h0, tm);
+    for (int w0 = 48; w0 >= 8; --w0) {
+      const int w = (int)std::min<int64_t>(w0, tv);
+      if (h * w > 1536) continue;
+      const double c = fused_cost(tm, tv, h, w);
+      if (bt == 0 || c < best * (1.0 - 1e-9)) {
+        best = c;
+        bt = h;
+        bv = w;
+      }
+    }
+  }
+}
+
 // Whether the fused variant runs pass 2 once over all N tokens: dx in fp32 (dx is its own
 // accumulator) and N rows of x and of dx within the kernels' 32-bit buffer offsets.
 bool fused_pass2_over_all(const flce_config_t& cfg, int64_t N, int64_t H) {
@@ -260,12 +317,9 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (p.fused && grads) {   // pass 2: dlogits block slots for one step (at most 1.5 GiB)
     p.fused_all = fused_pass2_over_all(cfg, N, H);
     const int64_t tm = cdiv(p.fused_all ? N : p.C, kTile);
-    p.fused_bt = (int)std::min<int64_t>(flce::kFusedBlockTiles, tm);
-    p.fused_bv = (int)std::min<int64_t>(flce::kFusedBlockTiles, p.tiles_v);
+    fused_block_shape(tm, p.tiles_v, p.fused_bt, p.fused_bv);
     p.fused_slot_bytes = (int64_t)p.fused_bt * p.fused_bv * kTile * kTile * 2;
-    const int64_t blocks = cdiv(tm, p.fused_bt) * cdiv(p.tiles_v, p.fused_bv);
-    p.fused_slots =
-        (int)std::max<int64_t>(1, std::min<int64_t>(blocks, flce::kFusedSlotBudget / p.fused_slot_bytes));
+    p.fused_slots = (int)fused_slots_for(tm, p.tiles_v, p.fused_bt, p.fused_bv);
     off = align_up(off + (size_t)p.fused_slots * (size_t)p.fused_slot_bytes);
   }
   if (rms) {   // the chunk's normalised rows, their fp32 dL/dx, rstd, dgamma partials and sum

@@ -182,7 +182,6 @@ __host__ __device__ inline void step_items(const StepPlan& sp, int g, int w, F&&
   }
 }
 
-constexpr int kFusedBlockTiles = 16;   // block side in tiles (4096 tokens / vocabulary ids)
 constexpr int64_t kFusedSlotBudget = (int64_t)3 << 29;   // 1.5 GiB of dlogits slots per step
 constexpr int kFusedGrid = 256;        // workgroups of each pass-2 kernel
 
