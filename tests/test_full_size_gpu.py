@@ -12,9 +12,12 @@ Frobenius error <= 2e-2 (bf16 inputs), and the same bound on the dW rows no
 target hits (there dW is the softmax part alone, which the one-hot part would
 otherwise hide); every lse within 1e-4 of the oracle's relative to max |lse|.
 
-The Llama-3-vocabulary workload also runs with fp32 gradients in both variants
-(the fused variant needs fp32 dW to stay within its memory bound) against the
-same oracle result.  The long-context workload (N = 131,072) compares the loss,
+Every workload also runs the fused variant with fp32 gradients (its benchmark
+configuration: with bf16 dW it would need an fp32 dW accumulator beyond its memory
+bound) against the same oracle result; its pass-2 block shape is planned per
+launch, so the workloads cover several shapes and step counts.  The
+Llama-3-vocabulary workload further runs the chunked variant with fp32 gradients
+and in a single chunk.  The long-context workload (N = 131,072) compares the loss,
 all lse and all of dW, and dx on five whole 4096-row blocks (the first two,
 two in the middle, the last), since its [N,H] fp64 dx alone would be 4.3 GB on
 the host and every dx row depends on its own token only.
@@ -94,12 +97,15 @@ def _check(got, want, t, V, what, capsys):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["llama2_vocab", "llama3_dp8_share", "llama3_tp8_share", "qwen3_vocab"])
 def test_full_size_vs_oracle(name, capsys):
+    import torch
     w = WORKLOADS[name]
-    _say(capsys, f"\n[full-size] {name}: N={w.N} H={w.H} V={w.V} chunk={w.chunk}, bf16 gradients")
+    _say(capsys, f"\n[full-size] {name}: N={w.N} H={w.H} V={w.V} chunk={w.chunk}")
     d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
-    got = _run(d, w.chunk)
+    runs = {"chunked bf16 grads": _run(d, w.chunk),
+            "fused fp32 grads": _run(d, w.chunk, variant=1, grads=torch.float32)}
     want = _oracle(d, capsys, name)
-    _check(got, want, d["t"], w.V, name, capsys)
+    for what, got in runs.items():
+        _check(got, want, d["t"], w.V, f"{name}, {what}", capsys)
 
 
 @pytest.mark.timeout(900)
@@ -135,13 +141,16 @@ def test_llama3_full_size_both_variants_vs_oracle(capsys):
 
 @pytest.mark.timeout(1200)
 def test_long_context_full_size_vs_oracle(capsys):
+    import torch
     w = WORKLOADS["long_context"]
-    _say(capsys, f"\n[full-size] long_context: N={w.N} H={w.H} V={w.V} chunk={w.chunk}, bf16 gradients")
+    _say(capsys, f"\n[full-size] long_context: N={w.N} H={w.H} V={w.V} chunk={w.chunk}")
     d = make_inputs(w.N, w.H, w.V, w.dtype, w.seed, w.targets)
     nb = w.N // BLOCK
     blocks = [0, 1, nb // 2 - 1, nb // 2, nb - 1]
     rows = np.concatenate([np.arange(b * BLOCK, (b + 1) * BLOCK) for b in blocks])
-    got = _run(d, w.chunk, dx_rows=rows)
+    runs = {"chunked bf16 grads": _run(d, w.chunk, dx_rows=rows),
+            "fused fp32 grads": _run(d, w.chunk, variant=1, grads=torch.float32, dx_rows=rows)}
     want = _oracle(d, capsys, "long_context", dx_blocks=blocks)
     assert np.array_equal(want["dx_rows"], rows)
-    _check(got, want, d["t"], w.V, "long_context", capsys)
+    for what, got in runs.items():
+        _check(got, want, d["t"], w.V, f"long_context, {what}", capsys)
