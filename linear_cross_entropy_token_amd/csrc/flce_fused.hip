@@ -2,10 +2,10 @@
 // fused path uses (accumulator clearing, fp32 -> bf16 output casts).
 //
 // Pass 1 (logits_lse without the logits store, then lse_combine) leaves the per-token
-// log-sum-exp.  Pass 2 never writes a logits or dlogits tensor of the chunk: it recomputes logits
-// tiles, turns them into dlogits on chip and adds the dx and dW contributions straight into fp32
-// accumulators (the reduction by atomic adds that the "Unsloth deep architecture" page's
-// streaming CE kernel uses).  The recomputation costs one extra forward product (8 N H V flops
+// log-sum-exp.  Pass 2 recomputes the logits block by block, turns them into dlogits in the
+// recompute's epilogue and adds the dx and dW contributions into fp32 accumulators (the reduction
+// by atomic adds that the "Unsloth deep architecture" page's streaming CE kernel uses); no [chunk, V]
+// logits tensor is ever written.  The recomputation costs one extra forward product (8 N H V flops
 // instead of 6 N H V).
 #include "flce_device.hpp"
 #include "flce_internal.hpp"
@@ -16,9 +16,9 @@ namespace flce {
 // Pass 2.  Each add of a 256 x 256 partial tile into dx or dW costs one fp32 atomic per element, and
 // an atomic cannot complete in an XCD's L2 (the eight L2s are not coherent with each other), so it
 // travels to the memory side: a kernel that added one partial per (token tile, vocabulary tile)
-// pair would make 2 rows V H / 256 adds per launch.  Here the plane is cut into blocks of up to
-// 16 x 16 tiles (4096 tokens x 4096 vocabulary ids), 16x fewer adds, done in steps of two kernels
-// (the dealing of blocks and items is StepPlan's, flce_internal.hpp):
+// pair would make 2 rows V H / 256 adds per launch.  Here the plane is cut into blocks of bt x bv
+// tiles (planned per launch, e.g. 32 x 42: 8192 tokens x 10,752 vocabulary ids, ~36x fewer adds),
+// done in steps of two kernels (the dealing of blocks and items is StepPlan's, flce_internal.hpp):
 //   Z (fused_z_kernel): each logits tile of the step's blocks is recomputed (contraction over H on
 //     the tile engine) and turned into dlogits G = (exp(z - lse) - onehot) * scale, stored bf16 in
 //     the block's slot (the dlogits tile of the FLCE page's step 2, for a block of tiles; slots are
@@ -29,7 +29,7 @@ namespace flce {
 //     page's streaming CE kernel).
 // The kernel boundary orders the slots' writes before their reads.  A group of workgroups (one
 // XCD's) works on one block at a time, so each slot row or column that a product reads is fetched
-// once into the XCD's L2 for the group's products of it (16 of them, one per slice of H).
+// once into the XCD's L2 for the group's products of it (one per 256-wide slice of H).
 // ---------------------------------------------------------------------------
 
 // Adds a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c] with

@@ -121,8 +121,8 @@ struct FinalizeArgs {
 };
 
 // Fused variant, pass 2.  The (token x vocabulary) plane of a launch is cut into blocks of bt x bv
-// tiles (up to 16 x 16: 4096 tokens x 4096 vocabulary ids), taken row by row (token blocks outer) in
-// steps of up to `slots` blocks.  Per step, two kernels:
+// tiles (planned per launch, at most 1536 tiles), taken row by row (token blocks outer) in steps of
+// up to `slots` blocks.  Per step, two kernels:
 //   Z: recompute every logits tile of the step's blocks and store it as bf16 dlogits in the block's
 //      slot buffer (bt 256 rows x bv 256 columns);
 //   P: form the blocks' dx tiles (slot rows times W, contraction over the block's vocabulary ids)
