@@ -174,17 +174,18 @@ def hipblaslt_yardstick(x, W, rows: int, reps: int = 10):
     return res
 
 
-def fused_record(flce, x, W, t, w, chunk, steps, ignore, reduction):
-    """The fused variant (two passes, no logits buffer) on the same inputs, fp32 gradients (with
-    bf16 dW its fp32 accumulator would be V H 4 bytes extra): ms per step, credited TFLOP/s
-    (6 N H V) and executed (8 N H V: the recompute), peak extra HBM, per-kernel averages."""
+def fused_record(flce, x, W, t, w, chunk, steps, ignore, reduction, grad_fp32=True):
+    """The fused variant (two passes, logits recomputed) on the same inputs: ms per step, credited
+    TFLOP/s (6 N H V) and executed (8 N H V: the recompute), peak extra HBM, per-kernel averages.
+    fp32 gradients give its fastest form (one pass 2 over all tokens, atomics into dx and dW);
+    bf16 gradients are the chunked line's own configuration (pass 2 per chunk, dW stored)."""
     import torch
     dev = x.device
-    f = flce.FusedLinearCrossEntropy(in_dtype=x.dtype, dx_dtype=torch.float32, dw_dtype=torch.float32,
-                                     variant=flce.FLCE_FUSED)
+    gdt = torch.float32 if grad_fp32 else x.dtype
+    f = flce.FusedLinearCrossEntropy(in_dtype=x.dtype, dx_dtype=gdt, dw_dtype=gdt, variant=flce.FLCE_FUSED)
     loss = torch.empty((), dtype=torch.float32, device=dev)
-    dx = torch.empty(x.shape, dtype=torch.float32, device=dev)
-    dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    dx = torch.empty(x.shape, dtype=gdt, device=dev)
+    dW = torch.empty(W.shape, dtype=gdt, device=dev)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
@@ -233,7 +234,8 @@ def fused_record(flce, x, W, t, w, chunk, steps, ignore, reduction):
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS["bf16"], 4),
                 "traffic": measured_traffic("fused_bwd", w.name, eff_chunk),
                 "flops_per_launch": fb["flops"] / fb["launches"], "avg_launch_ms": round(avg_s * 1e3, 4)}
-    return {"variant": "fused", "grad_dtype": "fp32", "steps": steps, "warmup": 1, "ms_per_step": round(ms, 4),
+    return {"variant": "fused", "grad_dtype": "fp32" if grad_fp32 else "bf16", "steps": steps, "warmup": 1,
+            "ms_per_step": round(ms, 4),
             "tokens_per_s": round(w.N / (ms * 1e-3), 1),
             "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
             "mfma_peak_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
@@ -423,6 +425,10 @@ def main():
                                                                args.accumulate or w.dtype != "bf16"):
         log(f"[bench] fused variant, fp32 gradients: {args.fused_steps} timed steps")
         fused = fused_record(flce, x, W, t, w, chunk, args.fused_steps, ignore, args.reduction)
+        log(f"[bench] fused variant, bf16 gradients: {args.fused_steps} timed steps")
+        fb = fused_record(flce, x, W, t, w, chunk, args.fused_steps, ignore, args.reduction, grad_fp32=False)
+        fused["bf16_grads"] = {k: fb[k] for k in ("ms_per_step", "tokens_per_s", "tflops", "mfma_peak_frac",
+                                                   "peak_extra_gb", "workspace_gb", "loss")}
     if not args.no_materialised:
         log("[bench] peak HBM of the materialised-logits PyTorch loss")
         extra["materialised_baseline"] = materialised_peak(x, W, t)

@@ -73,18 +73,19 @@ typedef enum {
   FLCE_CHUNKED = 0,           /* token chunks; one [C,V] buffer overwritten in place by dlogits */
   FLCE_FUSED = 1              /* two passes, logits recomputed: pass 1 per-token log-sum-exp (no
                                  logits stored); pass 2 cuts the (token x vocabulary) plane into
-                                 blocks of up to 4096 x 4096 and runs in steps: one kernel
-                                 recomputes the logits of up to 1.5 GiB of blocks and stores them
-                                 as dlogits in workspace slots, a second forms the blocks' dx and
-                                 dW tile products and adds them into fp32 accumulators with
-                                 atomics.  With fp32
-                                 dx, pass 2 runs once over all N tokens after every chunk's pass 1
-                                 (dx is its own accumulator); with bf16 dx, once per chunk into an
-                                 fp32 [chunk, H] accumulator.  bf16 inputs
-                                 only.  With bf16 dW the accumulator is an extra V*H*4 bytes; with
-                                 fp32 dW it is dW itself.  Results are not bitwise repeatable.
-                                 Size limit: (V + 256) * H * 4 and (chunk + 256) * H * 4 below
-                                 4 GiB (32-bit offsets into the accumulators), else UNSUPPORTED. */
+                                 blocks (planned per launch, at most 1536 tiles of 256 x 256) and
+                                 runs in steps: one kernel recomputes the logits of up to 1.5 GiB
+                                 of blocks and stores them as dlogits in workspace slots, a second
+                                 forms the blocks' dx and dW tile products and adds them into
+                                 fp32 accumulators with atomics.  With fp32 dx and dW, pass 2 runs
+                                 once over all N tokens after every chunk's pass 1 (dx and dW are
+                                 their own accumulators).  Otherwise it runs once per chunk: bf16
+                                 dx through an fp32 [chunk, H] accumulator; bf16 dW with one token
+                                 block per launch, so that each dW tile has one product per chunk
+                                 and is stored (added after the first chunk) with no accumulator.
+                                 bf16 inputs only.  Results are not bitwise repeatable.  Size
+                                 limit: (V + 256) * H * 4 and (chunk + 256) * H * 4 below 4 GiB
+                                 (32-bit offsets into the accumulators), else UNSUPPORTED. */
 } flce_variant_t;
 
 typedef struct {

@@ -39,12 +39,13 @@ struct Plan {
   int splits = 1;
   int64_t k_per_split = 0;
   size_t off_z = 0, off_pm = 0, off_ps = 0, off_zt = 0, off_lse = 0, off_loss = 0, off_part = 0;
-  size_t off_dxacc = 0, off_dwacc = 0;   // fused variant: fp32 accumulators for bf16 outputs
+  size_t off_dxacc = 0;                  // fused variant: fp32 dx accumulator of a chunk for bf16 dx
   size_t off_gbuf = 0;                   // fused variant: the workgroups' dlogits block buffers
   int fused_bt = 0, fused_bv = 0;        // fused variant: pass-2 block shape in tiles (tokens, vocabulary)
   int fused_slots = 0;                   // fused variant: dlogits block slots (blocks per pass-2 step)
   int64_t fused_slot_bytes = 0;          // fused variant: bytes per slot
   bool fused_all = false;                // fused variant: one pass 2 over all N (fp32 dx) instead of per chunk
+  bool fused_dw_owned = false;           // fused variant: bf16 dW stored by its one product per chunk (no accumulator)
   size_t off_scale = 0;                  // flce::Scale of the call
   size_t off_xc = 0, off_dxc = 0, off_rstd = 0, off_rpart = 0, off_dgacc = 0;   // RMSNorm path
   bool fused = false;
@@ -223,7 +224,7 @@ int64_t fused_slots_for(int64_t tm, int64_t tv, int bt, int bv) {
 // measured on the Llama-3, Qwen3, long-context and Llama-2 workloads (16 x 16, 32 x 16, 16 x 32,
 // 32 x 32 and 24 x 24 tiles), whose pass-2 times it orders correctly.
 constexpr double kAtomicWeight = 0.93;
-double fused_cost(int64_t tm, int64_t tv, int bt, int bv) {
+double fused_cost(int64_t tm, int64_t tv, int bt, int bv, bool dw_owned) {
   const int64_t bvn = cdiv(tv, bv), nb = cdiv(tm, bt) * bvn, slots = fused_slots_for(tm, tv, bt, bv);
   double total = 0.0;
   for (int64_t first = 0; first < nb; first += slots) {
@@ -234,7 +235,7 @@ double fused_cost(int64_t tm, int64_t tv, int bt, int bv) {
       for (int64_t j = g; j < count; j += 8) {
         const int64_t b = first + j, r = b / bvn, c = b - r * bvn;
         const double nt = (double)std::min<int64_t>(bt, tm - r * bt), nv = (double)std::min<int64_t>(bv, tv - c * bv);
-        w += nt * nv + kAtomicWeight * (nt + nv);
+        w += nt * nv + kAtomicWeight * (dw_owned ? nt : nt + nv);
       }
       worst = std::max(worst, w);
     }
@@ -243,18 +244,19 @@ double fused_cost(int64_t tm, int64_t tv, int bt, int bv) {
   return total;
 }
 
-// Block shape of pass 2: heights of 32, 16 or 8 token tiles, widths of 8 .. 48 vocabulary tiles, at
-// most 1536 tiles (192 MiB of slot, so that a step holds at least 8 blocks); the cheapest under
-// fused_cost, the larger block (fewer atomics) on a tie.
-void fused_block_shape(int64_t tm, int64_t tv, int& bt, int& bv) {
+// Block shape of pass 2: heights of 32, 16 or 8 token tiles (dw_owned: all tm of the launch, one
+// token block), widths of 8 .. 48 vocabulary tiles (dw_owned: 1 .. 96), at most 1536 tiles (192 MiB
+// of slot, so that a step holds at least 8 blocks); the cheapest under fused_cost, the larger block
+// (fewer atomics) on a tie.
+void fused_block_shape(int64_t tm, int64_t tv, bool dw_owned, int& bt, int& bv) {
   double best = 0.0;
   bt = bv = 0;
   for (const int h0 : {32, 16, 8}) {
-    const int h = (int)std::min<int64_t>(h0, tm);
-    for (int w0 = 48; w0 >= 8; --w0) {
+    const int h = dw_owned ? (int)tm : (int)std::min<int64_t>(h0, tm);
+    for (int w0 = dw_owned ? 96 : 48; w0 >= (dw_owned ? 1 : 8); --w0) {
       const int w = (int)std::min<int64_t>(w0, tv);
       if (h * w > 1536) continue;
-      const double c = fused_cost(tm, tv, h, w);
+      const double c = fused_cost(tm, tv, h, w, dw_owned);
       if (bt == 0 || c < best * (1.0 - 1e-9)) {
         best = c;
         bt = h;
@@ -311,13 +313,14 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   if (!p.fused && grads && p.splits > 1) off = align_up(off + (size_t)p.splits * p.C * H * sizeof(float));
   p.off_dxacc = off;
   if (p.fused && grads && cfg.dx_dtype == FLCE_BF16) off = align_up(off + (size_t)p.C * H * sizeof(float));
-  p.off_dwacc = off;
-  if (p.fused && grads && cfg.dw_dtype == FLCE_BF16) off = align_up(off + (size_t)V * H * sizeof(float));
+  // bf16 dW: pass 2 per chunk with one token block per launch, so that every dW tile has one product
+  // per chunk and is stored (added, after the first chunk) into dW directly: no V x H fp32 accumulator
+  p.fused_dw_owned = p.fused && grads && cfg.dw_dtype == FLCE_BF16;
   p.off_gbuf = off;
   if (p.fused && grads) {   // pass 2: dlogits block slots for one step (at most 1.5 GiB)
-    p.fused_all = fused_pass2_over_all(cfg, N, H);
+    p.fused_all = fused_pass2_over_all(cfg, N, H) && !p.fused_dw_owned;
     const int64_t tm = cdiv(p.fused_all ? N : p.C, kTile);
-    fused_block_shape(tm, p.tiles_v, p.fused_bt, p.fused_bv);
+    fused_block_shape(tm, p.tiles_v, p.fused_dw_owned, p.fused_bt, p.fused_bv);
     p.fused_slot_bytes = (int64_t)p.fused_bt * p.fused_bv * kTile * kTile * 2;
     p.fused_slots = (int)fused_slots_for(tm, p.tiles_v, p.fused_bt, p.fused_bv);
     off = align_up(off + (size_t)p.fused_slots * (size_t)p.fused_slot_bytes);
@@ -678,11 +681,12 @@ flce_status_t run_rmsnorm(const Exec& e, const Plan& p, const Opts& o, const voi
 // Pass 2 of the fused variant over `rows` tokens starting at token s: the (token x vocabulary)
 // plane in blocks of the plan's shape, in steps of up to fused_slots blocks, each step a Z kernel
 // (dlogits of its blocks into the slots) and a P kernel (dx and dW tile products from the slots,
-// added into dx_acc (rows x H, fp32) and dw_acc (V x H, fp32) with atomics).  A launch over fewer
-// tokens than the plan's (the last chunk) has fewer blocks of the same shape.
+// added into dx_acc (rows x H, fp32) with atomics, and into dw_acc (V x H, fp32) with atomics or,
+// with one token block per launch (fused_dw_owned), stored into dW).  A launch over fewer tokens than
+// the plan's (the last chunk) has fewer blocks of the same shape.
 flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t s, int64_t rows, const void* x,
                            const void* W, const int64_t* t, const float* lse, float* dx_acc, float* dw_acc,
-                           hipStream_t st) {
+                           void* dW, hipStream_t st) {
   const double VH = (double)p.V * (double)p.H;
   flce::FusedStepArgs fa{};
   fa.x = static_cast<const char*>(x) + (size_t)s * p.H * 2;
@@ -691,6 +695,10 @@ flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t 
   fa.lse = lse + s;
   fa.dx_acc = dx_acc;
   fa.dw_acc = dw_acc;
+  fa.dw_out = dW;
+  fa.dw_owned = p.fused_dw_owned ? 1 : 0;
+  fa.dw_fp32 = e.h->cfg.dw_dtype == FLCE_FP32 ? 1 : 0;
+  fa.dw_add = (s > 0 || o.accumulate) ? 1 : 0;   // dw_owned: the first chunk overwrites dW
   fa.slots = e.ws + p.off_gbuf;
   fa.slot_bytes = p.fused_slot_bytes;
   fa.rows = (int)rows;
@@ -732,14 +740,15 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
   float* lse = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(ws + p.off_lse);
   float* loss_rows = reinterpret_cast<float*>(ws + p.off_loss);
   const bool dx32 = cfg.dx_dtype == FLCE_FP32, dw32 = cfg.dw_dtype == FLCE_FP32;
-  float* dw_acc = dw32 ? static_cast<float*>(dW) : reinterpret_cast<float*>(ws + p.off_dwacc);
+  // fp32 dW is its own atomic accumulator; bf16 dW is stored by its one product per chunk
+  float* dw_acc = dw32 ? static_cast<float*>(dW) : nullptr;
   const flce::Scale* scale = reinterpret_cast<const flce::Scale*>(ws + p.off_scale);
   const double VH = (double)p.V * (double)p.H;
   const flce_status_t sc = launch_scale(e, p, o, t, st);
   if (sc != FLCE_OK) return sc;
 
   // fp32 outputs are the accumulators themselves: cleared unless the call accumulates into them
-  if (o.grads && !(dw32 && o.accumulate)) {
+  if (o.grads && !p.fused_dw_owned && !o.accumulate) {
     flce::FillArgs zw{dw_acc, p.V * p.H};
     FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * VH, st));
     FLCE_LAUNCH(flce::launch_fill_zero(zw, st));
@@ -796,7 +805,7 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
       FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
     }
-    const flce_status_t r = launch_pass2(e, p, o, s, rows, x, W, t, lse, dx_acc, dw_acc, st);
+    const flce_status_t r = launch_pass2(e, p, o, s, rows, x, W, t, lse, dx_acc, dw_acc, dW, st);
     if (r != FLCE_OK) return r;
     if (!dx32) {
       flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
@@ -805,13 +814,8 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
     }
   }
   if (o.grads && p.fused_all) {
-    const flce_status_t r = launch_pass2(e, p, o, 0, p.N, x, W, t, lse, static_cast<float*>(dx), dw_acc, st);
+    const flce_status_t r = launch_pass2(e, p, o, 0, p.N, x, W, t, lse, static_cast<float*>(dx), dw_acc, dW, st);
     if (r != FLCE_OK) return r;
-  }
-  if (o.grads && !dw32) {
-    flce::CastArgs cw{dw_acc, dW, p.V * p.H, o.accumulate};
-    FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * VH, st));
-    FLCE_LAUNCH(flce::launch_cast_bf16(cw, st));
   }
   flce::FinalizeArgs fa{};
   fa.loss_rows = loss_rows;

@@ -59,6 +59,40 @@ __device__ __forceinline__ void atomic_add_tile(const f32x16 (&acc)[kColBlocks][
   }
 }
 
+// Stores a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c]
+// (fp32 or bf16, round to nearest even), adding the value already there when `add`; rows >= row_end
+// and columns >= H are skipped.  For tiles with exactly one producer (no other workgroup writes them).
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[kColBlocks][4], void* out, int row0, int row_end,
+                                           int col0, int H, bool fp32, bool add) {
+  const int tid = opaque_tid();
+  const Frag f = frag_coords(tid);
+  const int ol = tid & 63;
+  const int row_l = f.rowb + 4 * (ol >> 5);   // + 32 j + 8 (rg / 4) + rg % 4
+#pragma unroll
+  for (int i = 0; i < kColBlocks; ++i) {
+    const int col = col0 + f.colb + 32 * i + (ol & 31);
+    if (col >= H) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rg = 0; rg < 16; ++rg) {
+        const int row = row0 + row_l + 32 * j + 8 * (rg >> 2) + (rg & 3);
+        if (row >= row_end) continue;
+        const int64_t e = (int64_t)row * H + col;
+        float v = acc[i][j][rg];
+        if (fp32) {
+          float* p = static_cast<float*>(out) + e;
+          if (add) v += *p;
+          *p = v;
+        } else {
+          bf16_t* p = static_cast<bf16_t*>(out) + e;
+          if (add) v += bf16_to_f32(*p);
+          *p = f32_to_bf16(v);
+        }
+      }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void fused_z_kernel(FusedStepArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kDeepRingBytes];
   const StepPlan& sp = a.sp;
@@ -179,8 +213,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_p_kernel(FusedStepArgs a) {
         R.init(G, gld, nj * kTile, nvoc, gbytes);
         gemm_tile<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, false>, true>(acc, smem, C, R, 0, ntok,
                                                                          opaque_tid());
-        atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V,
-                        hb * kTile, a.H);
+        if (a.dw_owned)   // the block holds every token of the launch: this is the tile's only product
+          store_tile(acc, a.dw_out, voc0 + nj * kTile, a.V, hb * kTile, a.H, a.dw_fp32 != 0, a.dw_add != 0);
+        else
+          atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V,
+                          hb * kTile, a.H);
       }
     }
     seen += n;

@@ -111,8 +111,8 @@ def test_full_size_vs_oracle(name, capsys):
 @pytest.mark.timeout(900)
 def test_llama3_full_size_both_variants_vs_oracle(capsys):
     """The benchmark workload: chunked with bf16 gradients (the benchmark's configuration, and
-    again in a single chunk of all tokens), then chunked and fused with fp32 gradients, all
-    against one oracle result.  On fp32 outputs the
+    again in a single chunk of all tokens), then chunked and fused with fp32 gradients and fused
+    with bf16 gradients, all against one oracle result.  On fp32 outputs the
     exact invariants of the definition hold as well: dW's column sums vanish (every G row sums
     to zero) and <x,dx> = <W,dW> (z = x W^T is bilinear)."""
     import torch
@@ -124,7 +124,9 @@ def test_llama3_full_size_both_variants_vs_oracle(capsys):
             # 32-bit offset limit, so its last rows sit at the largest offsets of every launch
             "chunked bf16 grads, one chunk": _run(d, w.N),
             "chunked fp32 grads": _run(d, w.chunk, grads=torch.float32),
-            "fused fp32 grads": _run(d, w.chunk, variant=1, grads=torch.float32)}
+            "fused fp32 grads": _run(d, w.chunk, variant=1, grads=torch.float32),
+            # bf16 dx and dW, the chunked benchmark configuration: dW stored once per chunk
+            "fused bf16 grads": _run(d, w.chunk, variant=1)}
     want = _oracle(d, capsys, "llama3_vocab")
     for what, got in runs.items():
         _check(got, want, d["t"], w.V, what, capsys)

@@ -24,12 +24,16 @@ def _gpu():
 
 
 CASES = [
-    # id, N, H, V, chunk, grads fp32
-    ("ragged", 1000, 512, 5000, 384, False),
-    ("ragged_fp32_grads", 1000, 512, 5000, 384, True),
-    ("N1", 1, 64, 1001, 0, False),
-    ("H64_V1001", 300, 64, 1001, 128, False),
-    ("one_chunk", 512, 256, 3000, 0, True),
+    # id, N, H, V, chunk, fp32 gradients: "" (bf16 dx and dW: pass 2 per chunk, dW stored by its one
+    # product), "dx+dW" (one pass 2 over all tokens, atomics into both), "dx" or "dW" (per chunk)
+    ("ragged", 1000, 512, 5000, 384, ""),
+    ("ragged_fp32_grads", 1000, 512, 5000, 384, "dx+dW"),
+    ("ragged_fp32_dx_bf16_dW", 1000, 512, 5000, 384, "dx"),
+    ("ragged_bf16_dx_fp32_dW", 1000, 512, 5000, 384, "dW"),
+    ("N1", 1, 64, 1001, 0, ""),
+    ("H64_V1001", 300, 64, 1001, 128, ""),
+    ("H320_V2049", 700, 320, 2049, 256, ""),
+    ("one_chunk", 512, 256, 3000, 0, "dx+dW"),
 ]
 
 
@@ -38,10 +42,25 @@ def test_fused_small_vs_oracle(case):
     import torch
     name, N, H, V, chunk, g32 = case
     d = make_inputs(N, H, V, "bf16", seed=N + V)
-    gd = torch.float32 if g32 else None
-    got = run_flce(d, chunk=chunk, dx_dtype=gd, dw_dtype=gd, variant=FUSED)
+    gx = torch.float32 if "dx" in g32 else None
+    gw = torch.float32 if "dW" in g32 else None
+    got = run_flce(d, chunk=chunk, dx_dtype=gx, dw_dtype=gw, variant=FUSED)
     got["handle"].close()
     compare(got, oracle_full(d), d["t"], V, 2e-2, 1e-4, "fused " + name)
+
+
+def test_fused_workspace_within_the_memory_bar():
+    """Peak extra HBM of the fused variant at the Llama-3 size stays within 2 GB for every gradient
+    dtype: bf16 dW is stored by its one product per chunk (no V x H fp32 accumulator)."""
+    import torch
+    from linear_cross_entropy_token_amd import FusedLinearCrossEntropy
+    w = WORKLOADS["llama3_vocab"]
+    for gx, gw in ((None, None), (torch.float32, None), (None, torch.float32), (torch.float32, torch.float32)):
+        f = FusedLinearCrossEntropy(dx_dtype=gx, dw_dtype=gw, variant=FUSED)
+        ws = f.workspace_bytes(w.N, w.H, w.V, w.chunk)
+        f.close()
+        print(f"[fused workspace] dx {gx} dW {gw}: {ws / 1e9:.3f} GB", flush=True)
+        assert 0 < ws <= 1.7e9
 
 
 def test_fused_full_vocab_reduced_tokens():
