@@ -697,7 +697,6 @@ flce_status_t launch_pass2(const Exec& e, const Plan& p, const Opts& o, int64_t 
   fa.dw_acc = dw_acc;
   fa.dw_out = dW;
   fa.dw_owned = p.fused_dw_owned ? 1 : 0;
-  fa.dw_fp32 = e.h->cfg.dw_dtype == FLCE_FP32 ? 1 : 0;
   fa.dw_add = (s > 0 || o.accumulate) ? 1 : 0;   // dw_owned: the first chunk overwrites dW
   fa.slots = e.ws + p.off_gbuf;
   fa.slot_bytes = p.fused_slot_bytes;

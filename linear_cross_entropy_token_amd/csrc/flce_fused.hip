@@ -59,36 +59,33 @@ __device__ __forceinline__ void atomic_add_tile(const f32x16 (&acc)[kColBlocks][
   }
 }
 
-// Stores a 256 x 256 fp32 tile in the SWAP accumulator layout into out[(row0 + r) H + col0 + c]
-// (fp32 or bf16, round to nearest even), adding the value already there when `add`; rows >= row_end
-// and columns >= H are skipped.  For tiles with exactly one producer (no other workgroup writes them).
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[kColBlocks][4], void* out, int row0, int row_end,
-                                           int col0, int H, bool fp32, bool add) {
-  const int tid = opaque_tid();
-  const Frag f = frag_coords(tid);
-  const int ol = tid & 63;
-  const int row_l = f.rowb + 4 * (ol >> 5);   // + 32 j + 8 (rg / 4) + rg % 4
+// Stores a 256 x 256 fp32 tile in the engine's default accumulator layout (each lane holds runs of 4
+// consecutive columns of one row) into out[(row0 + r) H + col0 + c] as bf16 (round to nearest even),
+// adding the bf16 value already there when `add`: 8-byte loads and stores.  Rows >= row_end and
+// columns >= H are skipped (H is a multiple of 8).  For tiles with exactly one producer.
+__device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[kColBlocks][4], bf16_t* out, int row0,
+                                                int row_end, int col0, int H, bool add) {
+  const Frag f = frag_coords(opaque_tid());
 #pragma unroll
-  for (int i = 0; i < kColBlocks; ++i) {
-    const int col = col0 + f.colb + 32 * i + (ol & 31);
-    if (col >= H) continue;
+  for (int j = 0; j < 4; ++j) {
+    const int row = row0 + f.row(j);
+    if (row >= row_end) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < kColBlocks; ++i)
 #pragma unroll
-      for (int rg = 0; rg < 16; ++rg) {
-        const int row = row0 + row_l + 32 * j + 8 * (rg >> 2) + (rg & 3);
-        if (row >= row_end) continue;
-        const int64_t e = (int64_t)row * H + col;
-        float v = acc[i][j][rg];
-        if (fp32) {
-          float* p = static_cast<float*>(out) + e;
-          if (add) v += *p;
-          *p = v;
-        } else {
-          bf16_t* p = static_cast<bf16_t*>(out) + e;
-          if (add) v += bf16_to_f32(*p);
-          *p = f32_to_bf16(v);
+      for (int q = 0; q < 4; ++q) {
+        const int col = col0 + f.col0(i, q);
+        if (col >= H) continue;
+        u32x2* p = reinterpret_cast<u32x2*>(out + (int64_t)row * H + col);
+        f32x4 v{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if (add) {
+          const u32x2 old = *p;
+          v[0] += bf16_to_f32(old[0] & 0xffffu);
+          v[1] += bf16_to_f32(old[0] >> 16);
+          v[2] += bf16_to_f32(old[1] & 0xffffu);
+          v[3] += bf16_to_f32(old[1] >> 16);
         }
+        *p = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
   }
 }
@@ -211,13 +208,15 @@ __global__ __launch_bounds__(kThreads, 1) void fused_p_kernel(FusedStepArgs a) {
         Operand<bf16_t, false> R;   // rows: G[token][nj*256 + v]
         C.init(X + (int64_t)tok0 * a.H, a.H, hb * kTile, a.H, (uint32_t)((int64_t)ntok * a.H * 2));
         R.init(G, gld, nj * kTile, nvoc, gbytes);
-        gemm_tile<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, false>, true>(acc, smem, C, R, 0, ntok,
-                                                                         opaque_tid());
-        if (a.dw_owned)   // the block holds every token of the launch: this is the tile's only product
-          store_tile(acc, a.dw_out, voc0 + nj * kTile, a.V, hb * kTile, a.H, a.dw_fp32 != 0, a.dw_add != 0);
-        else
+        if (a.dw_owned) {   // the block holds every token of the launch: this is the tile's only product
+          gemm_tile<bf16_t>(acc, smem, C, R, 0, ntok, opaque_tid());
+          store_tile_bf16(acc, static_cast<bf16_t*>(a.dw_out), voc0 + nj * kTile, a.V, hb * kTile, a.H, a.dw_add != 0);
+        } else {
+          gemm_tile<bf16_t, Operand<bf16_t, false>, Operand<bf16_t, false>, true>(acc, smem, C, R, 0, ntok,
+                                                                           opaque_tid());
           atomic_add_tile(acc, make_rsrc(a.dw_acc, (uint32_t)((int64_t)a.V * a.H * 4)), voc0 + nj * kTile, a.V,
                           hb * kTile, a.H);
+        }
       }
     }
     seen += n;

@@ -192,9 +192,8 @@ struct FusedStepArgs {
   const float* lse;     // their log-sum-exp [rows]
   float* dx_acc;        // fp32 [rows][H], cleared (or holding the values to add to) before the first step
   float* dw_acc;        // fp32 [V][H], cleared before the first launch of a call (dw_owned == 0)
-  void* dw_out;         // dw_owned: dW itself [V][H] (fp32 or bf16), stored (dw_add: added) by its one product
+  void* dw_out;         // dw_owned: dW itself [V][H] (bf16), stored (dw_add: added) by its one product
   int dw_owned;         // 1: one token block covers the launch, so each dW tile has one product: no atomics
-  int dw_fp32;          // dw_owned: dW is fp32 (else bf16)
   int dw_add;           // dw_owned: add into dW instead of overwriting it
   char* slots;          // [count][slot_bytes]: the step's dlogits blocks (bf16, bv 256 per row)
   int64_t slot_bytes;
