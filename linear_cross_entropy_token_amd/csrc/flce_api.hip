@@ -319,7 +319,8 @@ Plan make_plan(const flce_config_t& cfg, int64_t N, int64_t H, int64_t V, int64_
   p.off_gbuf = off;
   if (p.fused && grads) {   // pass 2: dlogits block slots for one step (at most 1.5 GiB)
     p.fused_all = fused_pass2_over_all(cfg, N, H) && !p.fused_dw_owned;
-    const int64_t tm = cdiv(p.fused_all ? N : p.C, kTile);
+    int64_t tm = cdiv(p.fused_all ? N : p.C, kTile);
+    if (p.fused_dw_owned) tm = std::min<int64_t>(tm, flce::kFusedOwnedMaxTiles);   // launches of <= this many
     fused_block_shape(tm, p.tiles_v, p.fused_dw_owned, p.fused_bt, p.fused_bv);
     p.fused_slot_bytes = (int64_t)p.fused_bt * p.fused_bv * kTile * kTile * 2;
     p.fused_slots = (int)fused_slots_for(tm, p.tiles_v, p.fused_bt, p.fused_bv);
@@ -804,8 +805,14 @@ flce_status_t run_fused(const Exec& e, const Plan& p, const Opts& o, const void*
       FLCE_LAUNCH(mark(e, K_FILL, 0.0, 4.0 * rows * p.H, st));
       FLCE_LAUNCH(flce::launch_fill_zero(zx, st));
     }
-    const flce_status_t r = launch_pass2(e, p, o, s, rows, x, W, t, lse, dx_acc, dw_acc, dW, st);
-    if (r != FLCE_OK) return r;
+    // with owned dW tiles a launch covers at most fused_bt token tiles (one token block): longer
+    // chunks take several launches, each storing (adding, after the call's first) its dW tiles
+    const int64_t span = p.fused_dw_owned ? (int64_t)p.fused_bt * kTile : (int64_t)rows;
+    for (int64_t u = 0; u < rows; u += span) {
+      const int64_t n = std::min<int64_t>(span, rows - u);
+      const flce_status_t r = launch_pass2(e, p, o, s + u, n, x, W, t, lse, dx_acc + (size_t)u * p.H, dw_acc, dW, st);
+      if (r != FLCE_OK) return r;
+    }
     if (!dx32) {
       flce::CastArgs cx{dx_acc, static_cast<char*>(dx) + (size_t)s * p.H * 2, (int64_t)rows * p.H, o.accumulate};
       FLCE_LAUNCH(mark(e, K_CAST, 0.0, 6.0 * rows * p.H, st));

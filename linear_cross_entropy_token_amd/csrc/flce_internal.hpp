@@ -184,6 +184,7 @@ __host__ __device__ inline void step_items(const StepPlan& sp, int g, int w, F&&
 
 constexpr int64_t kFusedSlotBudget = (int64_t)3 << 29;   // 1.5 GiB of dlogits slots per step
 constexpr int kFusedGrid = 256;        // workgroups of each pass-2 kernel
+constexpr int kFusedOwnedMaxTiles = 64;   // bf16 dW: token tiles per pass-2 launch (one token block, 16,384 tokens)
 
 struct FusedStepArgs {
   const void* x;        // first token row of the launch [rows][H] (bf16)

@@ -34,6 +34,10 @@ CASES = [
     ("H64_V1001", 300, 64, 1001, 128, ""),
     ("H320_V2049", 700, 320, 2049, 256, ""),
     ("one_chunk", 512, 256, 3000, 0, "dx+dW"),
+    # a 20,000-token chunk with bf16 dW: pass 2 in launches of at most 16,384 tokens (one token block
+    # each), the second adding into the dW tiles the first stored
+    ("long_chunk_bf16", 20000, 128, 3000, 20000, ""),
+    ("long_chunk_fp32_dx", 20000, 128, 3000, 20000, "dx"),
 ]
 
 
