@@ -62,3 +62,44 @@ def test_two_handles_on_two_streams():
         want = oracle_full(r["d"])
         got = {"loss": float(r["out"][0].item()), "dx": to_f64(r["out"][1]), "dW": to_f64(r["out"][2])}
         compare(got, want, r["d"]["t"], V, tol_grad=2e-2, what=f"N={N} H={H} V={V} C={C} dW={dw or 'bf16'}")
+
+
+def test_fused_and_chunked_handles_on_two_streams():
+    """A fused call (its pass-2 kernels hold no waits on other workgroups, so they may share the
+    device with any other kernel) overlapping a chunked call on another stream: both match the
+    oracle, and the chunked one is bitwise what it gives alone."""
+    import torch as _t
+    torch = require_gpu()
+    from linear_cross_entropy_token_amd import FusedLinearCrossEntropy, FLCE_FUSED
+    shapes = [(900, 264, 3000, 256), (1000, 512, 5000, 384)]
+    runs = []
+    for k, (N, H, V, C) in enumerate(shapes):
+        d = make_inputs(N, H, V, "bf16", seed=171 + k)
+        x, W, t = to_device(d)
+        fused = k == 1
+        f = FusedLinearCrossEntropy(variant=FLCE_FUSED if fused else 0,
+                                    dx_dtype=_t.float32 if fused else None, dw_dtype=_t.float32 if fused else None)
+        f.reserve(N, H, V, C)
+        gd = _t.float32 if fused else x.dtype
+        out = (torch.empty((), dtype=torch.float32, device="cuda"), torch.empty(x.shape, dtype=gd, device="cuda"),
+               torch.empty(W.shape, dtype=gd, device="cuda"), torch.empty(N, dtype=torch.float32, device="cuda"))
+        runs.append(dict(d=d, x=x, W=W, t=t, C=C, f=f, out=out, fused=fused))
+    _call(runs[0], torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    alone = [o.clone() for o in runs[0]["out"]]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for r, s in zip(runs, streams):
+        with torch.cuda.stream(s):
+            _call(r, s)
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for name, e, g in zip(("loss", "dx", "dW", "lse"), alone, runs[0]["out"]):
+        assert torch.equal(e, g), f"chunked call next to a fused one: {name} differs from the call alone"
+    for r, (N, H, V, C) in zip(runs, shapes):
+        assert r["f"].check() == 0
+        want = oracle_full(r["d"])
+        got = {"loss": float(r["out"][0].item()), "dx": to_f64(r["out"][1]), "dW": to_f64(r["out"][2])}
+        compare(got, want, r["d"]["t"], V, tol_grad=2e-2, what=f"{'fused' if r['fused'] else 'chunked'} N={N}")
