@@ -266,8 +266,9 @@ void fused_block_shape(int64_t tm, int64_t tv, bool dw_owned, int& bt, int& bv) 
   }
 }
 
-// Whether the fused variant runs pass 2 once over all N tokens: dx in fp32 (dx is its own
-// accumulator) and N rows of x and of dx within the kernels' 32-bit buffer offsets.
+// Whether the fused variant may run pass 2 once over all N tokens: dx in fp32 (dx is its own
+// accumulator) and N rows of x and of dx within the kernels' 32-bit buffer offsets (make_plan also
+// requires fp32 dW: bf16 dW takes pass 2 per chunk, one token block per launch).
 bool fused_pass2_over_all(const flce_config_t& cfg, int64_t N, int64_t H) {
   const int64_t lim = (int64_t)0xFFFFFF00 - 4096;
   return cfg.dx_dtype == FLCE_FP32 && N * H * 2 < lim && (N + kTile) * H * 4 < lim;
